@@ -1,0 +1,121 @@
+"""fp64 CPU oracle for the Gated DeltaNet token mixer.
+
+TEST INFRASTRUCTURE. Only tests/, the smoke check in __graft_entry__ and the
+benchmark's cpu_baseline leg may import or run anything in this package. The
+product library (linear_attention_sequence_02_amd) never imports it and shares
+no code with it.
+
+  recurrent(...)  token-by-token fp64 recurrence (gdn_recurrent.c), the
+                  reference every GPU result is compared with.
+  chunked(...)    fp64 chunked UT/WY form of the same rule (chunked.py), used
+                  only to check that the chunk algorithm equals the recurrence.
+
+Where the pages are silent (they state the rule in words only), the readings
+are: decay before the delta correction; read-out after the write; state
+element [i][j] = (value index, key index); V head h uses QK head
+h // (Hv // Hqk); the query scale is an argument (1.0 unless a test says
+otherwise); q and k arrive L2-normalised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_recurrent.c")
+_LIB = os.path.join(_HERE, "liboracle_gdn.so")
+_lock = threading.Lock()
+_lib = None
+
+_DT_CODE = {np.dtype(np.uint16): 0, np.dtype(np.float32): 1, np.dtype(np.float64): 2}
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (fp64, no fast-math, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O3", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                        "-shared", "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+            f = lib.gdn_oracle_recurrent
+            f.restype = ctypes.c_int
+            f.argtypes = ([ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 3 + [ctypes.c_int]
+                          + [ctypes.c_void_p] + [ctypes.c_int32] * 5 + [ctypes.c_double]
+                          + [ctypes.c_int32] * 2 + [ctypes.c_void_p] * 2 + [ctypes.c_int32] * 2)
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def recurrent(q, k, v, g, beta, s0=None, cu_seqlens=None, *, scale: float = 1.0,
+              heads=None, threads: int = 0, mutant: int = 0, return_threads: bool = False):
+    """Run the fp64 recurrence.
+
+    q, k: [T, Hqk, dk]; v: [T, Hv, dv] as uint16 (bf16 bits), float32 or float64.
+    g, beta: [T, Hv]; s0: [N, Hv, dv, dk] or None (zeros); all float32 or float64.
+    cu_seqlens: [N + 1] offsets (None: one sequence of length T).
+    heads: (h_begin, h_end) to compute only those V heads (default all).
+    Returns (out [T, nh, dv], final_state [N, nh, dv, dk]) in float64.
+    """
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DT_CODE:
+        raise TypeError("q, k, v must share one of uint16 (bf16 bits), float32, float64")
+    aux = np.float64 if np.asarray(g).dtype == np.float64 else np.float32
+    g = np.ascontiguousarray(g, dtype=aux)
+    beta = np.ascontiguousarray(beta, dtype=aux)
+    T, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    if s0 is not None:
+        s0 = np.ascontiguousarray(s0, dtype=aux)
+        assert s0.shape == (N, Hv, dv, dk), s0.shape
+    hb, he = (0, Hv) if heads is None else heads
+    nh = he - hb
+    out = np.zeros((T, nh, dv), dtype=np.float64)
+    fin = np.zeros((N, nh, dv, dk), dtype=np.float64)
+    used = _load().gdn_oracle_recurrent(
+        _ptr(q), _ptr(k), _ptr(v), _DT_CODE[q.dtype], _ptr(g), _ptr(beta), _ptr(s0),
+        _DT_CODE[np.dtype(aux)], _ptr(cu), N, Hqk, Hv, dk, dv, float(scale), hb, he,
+        _ptr(out), _ptr(fin), int(threads), int(mutant))
+    if used < 0:
+        raise ValueError("oracle rejected the arguments")
+    if return_threads:
+        return out, fin, used
+    return out, fin
+
+
+def rel_l2(x, ref) -> float:
+    """||x - ref||_2 / ||ref||_2 in fp64 (0 when both are zero)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = float(np.linalg.norm((x - ref).ravel()))
+    den = float(np.linalg.norm(ref.ravel()))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return num / den
+
+
+from .chunked import chunked  # noqa: E402,F401
