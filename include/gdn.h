@@ -1,0 +1,134 @@
+/*
+ * gdn.h - C ABI of libgdn, a Gated DeltaNet token mixer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer (page "Qwen3-Next-80B-A3B-Instruct" model card, section "Model
+ * Overview": Gated DeltaNet, 32 V heads and 16 QK heads, head dimension 128;
+ * page "Qwen3-Next and vLLM", section "Hybrid Attention": Gated DeltaNet is the
+ * linear-attention half of the hybrid layout) keeps, per sequence and V head,
+ * a d_v x d_k fp32 state S. For every token, in order:
+ *
+ *     alpha = exp(g)
+ *     S     = alpha * S                              decay
+ *     S     = S + beta * (v - S k) k^T               delta-rule write along the unit key k
+ *     out   = scale * S q                            read-out after the write
+ *
+ * V head h reads QK head h / (num_v_heads / num_qk_heads), so consecutive V
+ * heads share a QK head (the pages give only the head counts; this grouping is
+ * the library's reading).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major arrays
+ *     owned by the caller. The library never allocates, frees or keeps them.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *     asynchronously on it; no entry point synchronises with the host, so the
+ *     calls can be captured in a HIP graph. Results are ready when the stream
+ *     has reached the call.
+ *   - q and k must already be L2-normalised per token and head; g <= 0 and
+ *     finite; beta in [0, 1]. These preconditions are not checked.
+ *   - State element S[i][j]: i is the value index (0..d_v-1), j the key index.
+ *   - Argument errors are detected on the host before anything is enqueued
+ *     and return a non-zero status; nothing is launched then. No C++
+ *     exception crosses this interface.
+ *
+ * Supported shapes: GDN_BF16 requires d_k = d_v = 128; GDN_FP32 requires
+ * d_k = d_v in {16, 32, 64, 128}. num_v_heads must be a multiple of
+ * num_qk_heads.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1,   /* null required pointer, bad count or size */
+    GDN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (dtype / head size) */
+    GDN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    GDN_ERR_HIP = 4            /* a HIP launch failed (the status string has no detail) */
+} gdn_status_t;
+
+typedef enum {
+    GDN_BF16 = 0,   /* q, k, v and out are bfloat16 */
+    GDN_FP32 = 1    /* q, k, v and out are float */
+} gdn_dtype_t;
+/* g, beta and all states are float in both modes. */
+
+/*
+ * Bytes of device workspace gdn_prefill needs for these sizes (may be 0).
+ * Returns 0 as well for arguments gdn_prefill would reject.
+ */
+size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs,
+                                  int32_t num_qk_heads, int32_t num_v_heads,
+                                  int32_t d_k, int32_t d_v, gdn_dtype_t dtype);
+
+/*
+ * Chunked prefill over packed variable-length sequences (chunk size 64: the
+ * intra-chunk decay masks, the UT/WY transform of the beta-weighted
+ * (I - beta k k^T) factors by a triangular solve, and the inter-chunk state
+ * propagation the layer's description names).
+ *
+ *   q, k           [total_tokens, num_qk_heads, d_k]   dtype
+ *   v              [total_tokens, num_v_heads, d_v]    dtype
+ *   g, beta        [total_tokens, num_v_heads]         float (g = log alpha)
+ *   initial_state  [num_seqs, num_v_heads, d_v, d_k]   float, or NULL for zeros
+ *   cu_seqlens     [num_seqs + 1] int32 token offsets, device memory, starting
+ *                  at 0, non-decreasing, ending at total_tokens; or NULL for one
+ *                  sequence of total_tokens tokens (num_seqs must be 1).
+ *                  Sequences may be empty (their final state is their initial
+ *                  state). Offsets are read on the device and are a
+ *                  precondition, not checked.
+ *   out            [total_tokens, num_v_heads, d_v]    dtype, written
+ *   final_state    [num_seqs, num_v_heads, d_v, d_k]   float, written; or NULL.
+ *                  May be the same pointer as initial_state (each state slice
+ *                  is read before it is overwritten); any other overlap with
+ *                  an input is undefined.
+ *   workspace      device buffer of at least gdn_prefill_workspace_size(...)
+ *                  bytes (NULL allowed when that size is 0). Its contents
+ *                  need no initialisation; concurrent calls need separate
+ *                  workspaces.
+ * total_tokens = 0 is allowed (only the states are copied).
+ */
+gdn_status_t gdn_prefill(const void* q, const void* k, const void* v,
+                         const float* g, const float* beta,
+                         const float* initial_state,
+                         const int32_t* cu_seqlens, int32_t num_seqs,
+                         int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads,
+                         int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype,
+                         void* out, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step for num_seqs independent sequences, one token each; the
+ * state is read and updated in place (the per-sequence recurrent state a
+ * serving engine's hybrid cache keeps for a linear-attention layer).
+ *
+ *   q, k     [num_seqs, num_qk_heads, d_k]   dtype
+ *   v        [num_seqs, num_v_heads, d_v]    dtype
+ *   g, beta  [num_seqs, num_v_heads]         float
+ *   state    [num_seqs, num_v_heads, d_v, d_k] float, updated in place
+ *   out      [num_seqs, num_v_heads, d_v]    dtype, written
+ * num_seqs = 0 is allowed (nothing is launched).
+ */
+gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, float* state,
+                             int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads,
+                             int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype,
+                             void* out, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* gdn_status_string(gdn_status_t status);
+
+/* Static, NUL-terminated build description (library version and GPU target). */
+const char* gdn_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,161 @@
+"""Python binding of libgdn, the Gated DeltaNet token mixer for MI355X (gfx950).
+
+The functions carry the C ABI's names (include/gdn.h) and only marshal
+arguments: torch tensors supply device pointers and the current HIP stream,
+every step of the layer runs in the library's kernels. There is no CPU or
+PyTorch fallback: if libgdn.so is missing or a call fails, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["gdn_prefill", "gdn_decode_step", "gdn_prefill_workspace_size", "gdn_status_string",
+           "gdn_build_info", "GDN_BF16", "GDN_FP32", "GdnError", "library_path"]
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(5)
+GDN_BF16, GDN_FP32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libgdn.so")
+_lock = threading.Lock()
+_lib = None
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {gdn_status_string(status)} (status {status})")
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(library_path):
+                raise RuntimeError(f"libgdn.so not built at {library_path}; run "
+                                   "`python -m linear_attention_sequence_02_amd.build`")
+            lib = ctypes.CDLL(library_path)
+            lib.gdn_prefill_workspace_size.restype = _sz
+            lib.gdn_prefill_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, ctypes.c_int]
+            lib.gdn_prefill.restype = ctypes.c_int
+            lib.gdn_prefill.argtypes = ([_vp] * 7 + [_i32, _i64, _i32, _i32, _i32, _i32, _f32, ctypes.c_int]
+                                        + [_vp, _vp, _vp, _sz, _vp])
+            lib.gdn_decode_step.restype = ctypes.c_int
+            lib.gdn_decode_step.argtypes = [_vp] * 6 + [_i32] * 5 + [_f32, ctypes.c_int, _vp, _vp]
+            lib.gdn_status_string.restype = ctypes.c_char_p
+            lib.gdn_status_string.argtypes = [ctypes.c_int]
+            lib.gdn_build_info.restype = ctypes.c_char_p
+            lib.gdn_build_info.argtypes = []
+            _lib = lib
+    return _lib
+
+
+def gdn_status_string(status: int) -> str:
+    return _load().gdn_status_string(int(status)).decode()
+
+
+def gdn_build_info() -> str:
+    return _load().gdn_build_info().decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_FP32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def gdn_prefill_workspace_size(total_tokens: int, num_seqs: int, num_qk_heads: int, num_v_heads: int,
+                               d_k: int, d_v: int, dtype: int) -> int:
+    return int(_load().gdn_prefill_workspace_size(total_tokens, num_seqs, num_qk_heads, num_v_heads,
+                                                  d_k, d_v, dtype))
+
+
+def gdn_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, scale: float = 1.0,
+                out=None, final_state=None, output_final_state: bool = True, workspace=None, stream=None):
+    """Chunked prefill. Shapes as in include/gdn.h; returns (out, final_state).
+
+    q, k [T, Hqk, d] and v [T, Hv, d] (bf16 or fp32, one dtype), g and beta
+    [T, Hv] fp32, initial_state [N, Hv, d, d] fp32 or None, cu_seqlens [N + 1]
+    int32 on the device or None (one sequence). Missing outputs and the
+    workspace are allocated with torch; pass them to avoid allocation.
+    """
+    dev = q.device
+    _check(q, "q", device=dev)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, q.dtype, dev)
+    for name, t in (("g", g), ("beta", beta), ("initial_state", initial_state)):
+        _check(t, name, torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    T, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    n = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    if out is None:
+        out = torch.empty((T, hv, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", q.dtype, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, hv, dv, dk), dtype=torch.float32, device=dev)
+    _check(final_state, "final_state", torch.float32, dev)
+    need = gdn_prefill_workspace_size(T, n, hqk, hv, dk, dv, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _load().gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                             _ptr(cu_seqlens), n, T, hqk, hv, dk, dv, float(scale), dt, _ptr(out),
+                             _ptr(final_state), _ptr(workspace), ws_bytes, _stream(stream, dev))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_prefill")
+    return out, final_state
+
+
+def gdn_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, out=None, stream=None):
+    """One decode step, state [N, Hv, d, d] fp32 updated in place; returns out [N, Hv, d]."""
+    dev = q.device
+    _check(q, "q", device=dev)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, q.dtype, dev)
+    for name, t in (("g", g), ("beta", beta), ("state", state)):
+        _check(t, name, torch.float32, dev)
+    N, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    if out is None:
+        out = torch.empty((N, hv, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", q.dtype, dev)
+    st = _load().gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), N, hqk, hv,
+                                 dk, dv, float(scale), dt, _ptr(out), _stream(stream, dev))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_decode_step")
+    return out

@@ -1,0 +1,97 @@
+// C ABI of libgdn (declarations and contracts in include/gdn.h).
+//
+// Host side only: argument validation, workspace accounting and kernel
+// dispatch on the caller's stream. No allocation, no host synchronisation.
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+bool fp32_head_size_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+gdn_status_t check_heads(int32_t hqk, int32_t hv, int32_t dk, int32_t dv, gdn_dtype_t dt) {
+    if (hqk <= 0 || hv <= 0 || dk <= 0 || dv <= 0) return GDN_ERR_INVALID_ARG;
+    if (hv % hqk != 0) return GDN_ERR_INVALID_ARG;
+    if (dt != GDN_BF16 && dt != GDN_FP32) return GDN_ERR_INVALID_ARG;
+    if (dk != dv) return GDN_ERR_UNSUPPORTED;
+    if (dt == GDN_BF16 && dk != 128) return GDN_ERR_UNSUPPORTED;
+    if (dt == GDN_FP32 && !fp32_head_size_ok(dk)) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+gdn_status_t hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t num_qk_heads,
+                                  int32_t num_v_heads, int32_t d_k, int32_t d_v, gdn_dtype_t dtype) {
+    if (total_tokens < 0 || num_seqs < 0) return 0;
+    if (check_heads(num_qk_heads, num_v_heads, d_k, d_v, dtype) != GDN_OK) return 0;
+    if (dtype == GDN_FP32) return 0;
+    return gdn::prefill_bf16_workspace_bytes(total_tokens, num_seqs, num_qk_heads, num_v_heads);
+}
+
+gdn_status_t gdn_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                         int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k,
+                         int32_t d_v, float scale, gdn_dtype_t dtype, void* out, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    gdn_status_t st = check_heads(num_qk_heads, num_v_heads, d_k, d_v, dtype);
+    if (st != GDN_OK) return st;
+    if (total_tokens < 0 || num_seqs < 0) return GDN_ERR_INVALID_ARG;
+    if (total_tokens > INT32_MAX) return GDN_ERR_UNSUPPORTED;   // cu_seqlens are int32
+    if (cu_seqlens == nullptr && num_seqs != 1) return GDN_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_INVALID_ARG;
+    if (num_seqs == 0) return GDN_OK;
+    const size_t need = gdn_prefill_workspace_size(total_tokens, num_seqs, num_qk_heads, num_v_heads,
+                                                   d_k, d_v, dtype);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
+    if (total_tokens == 0 && final_state == nullptr) return GDN_OK;
+
+    gdn::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.initial_state = initial_state; a.cu_seqlens = cu_seqlens; a.final_state = final_state;
+    a.out = out; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.total_tokens = total_tokens; a.num_seqs = num_seqs; a.num_qk_heads = num_qk_heads;
+    a.num_v_heads = num_v_heads; a.d = d_k; a.scale = scale; a.bf16 = (dtype == GDN_BF16);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(a.bf16 ? gdn::launch_prefill_bf16(a, s) : gdn::launch_prefill_f32(a, s));
+}
+
+gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             float* state, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads,
+                             int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype, void* out,
+                             void* stream) {
+    if (num_qk_heads <= 0 || num_v_heads <= 0 || d_k <= 0 || d_v <= 0 || num_seqs < 0)
+        return GDN_ERR_INVALID_ARG;
+    if (num_v_heads % num_qk_heads != 0) return GDN_ERR_INVALID_ARG;
+    if (dtype != GDN_BF16 && dtype != GDN_FP32) return GDN_ERR_INVALID_ARG;
+    if (d_k != d_v || !fp32_head_size_ok(d_k)) return GDN_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return GDN_OK;
+    if (!q || !k || !v || !g || !beta || !state || !out) return GDN_ERR_INVALID_ARG;
+    if ((int64_t)num_seqs * num_v_heads > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    gdn::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.out = out;
+    a.num_seqs = num_seqs; a.num_qk_heads = num_qk_heads; a.num_v_heads = num_v_heads; a.d = d_k;
+    a.scale = scale; a.bf16 = (dtype == GDN_BF16);
+    return hip_status(gdn::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+const char* gdn_status_string(gdn_status_t s) {
+    switch (s) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG: invalid argument";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: dtype or head size not supported";
+        case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP: HIP kernel launch failed";
+        default: return "GDN: unknown status";
+    }
+}
+
+const char* gdn_build_info(void) { return "libgdn 0.1 gfx950 (MI355X)"; }
+
+}  // extern "C"

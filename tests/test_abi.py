@@ -1,0 +1,124 @@
+"""The C ABI library loads, exports what include/gdn.h declares, and rejects bad
+arguments on the host. Every call here fails validation (or has nothing to do)
+before any kernel is enqueued, so these run without a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_attention_sequence_02_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.library_path):
+        pytest.fail("libgdn.so is not built (run __graft_entry__.build())")
+    return gdn._load()
+
+
+def test_header_declares_the_entry_points():
+    assert set(declared_functions()) == {"gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step",
+                                         "gdn_status_string", "gdn_build_info"}
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.library_path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT\s+(\S+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert gdn.gdn_status_string(s).startswith("GDN_")
+    assert "unknown" in gdn.gdn_status_string(99)
+    assert "gfx950" in gdn.gdn_build_info()
+
+
+def test_workspace_size(lib):
+    ws = gdn.gdn_prefill_workspace_size
+    assert ws(65536, 1, 16, 32, 128, 128, gdn.GDN_BF16) > 0
+    assert ws(65536, 1, 16, 32, 128, 128, gdn.GDN_FP32) == 0
+    assert ws(65536, 1, 3, 32, 128, 128, gdn.GDN_BF16) == 0          # rejected shape
+    assert ws(-1, 1, 16, 32, 128, 128, gdn.GDN_BF16) == 0
+    # grows with tokens and sequences (one chunk slot per 64 tokens plus one per sequence)
+    assert ws(64 * 10, 1, 16, 32, 128, 128, 0) < ws(64 * 10, 5, 16, 32, 128, 128, 0) < ws(64 * 20, 5, 16, 32, 128, 128, 0)
+
+
+def _prefill(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, cu=FAKE, n=2, T=100, hqk=16, hv=32, dk=128,
+             dv=128, scale=1.0, dt=gdn.GDN_BF16, out=FAKE, fin=FAKE, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(over)
+    return lib.gdn_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["n"], a["T"],
+                           a["hqk"], a["hv"], a["dk"], a["dv"], a["scale"], a["dt"], a["out"], a["fin"],
+                           a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(hqk=3), gdn.GDN_ERR_INVALID_ARG),                 # Hv not a multiple of Hqk
+    (dict(hqk=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dk=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(T=-5), gdn.GDN_ERR_INVALID_ARG),
+    (dict(n=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dt=7), gdn.GDN_ERR_INVALID_ARG),
+    (dict(q=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(out=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(cu=None, n=2), gdn.GDN_ERR_INVALID_ARG),          # no offsets needs exactly one sequence
+    (dict(dk=64, dv=64), gdn.GDN_ERR_UNSUPPORTED),          # bf16 path is d = 128
+    (dict(dk=128, dv=64), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dt=gdn.GDN_FP32, dk=48, dv=48), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(ws=None), gdn.GDN_ERR_WORKSPACE),
+    (dict(wsb=1024), gdn.GDN_ERR_WORKSPACE),
+    (dict(T=1 << 33), gdn.GDN_ERR_UNSUPPORTED),             # int32 offsets
+])
+def test_prefill_rejects(lib, over, status):
+    assert _prefill(lib, **over) == status
+
+
+def test_prefill_with_no_sequences_is_a_no_op(lib):
+    assert _prefill(lib, n=0) == gdn.GDN_OK
+
+
+def _decode(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, n=4, hqk=16, hv=32, dk=128, dv=128,
+             scale=1.0, dt=gdn.GDN_BF16, out=FAKE, stream=None)
+    a.update(over)
+    return lib.gdn_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"], a["n"], a["hqk"],
+                               a["hv"], a["dk"], a["dv"], a["scale"], a["dt"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(hqk=5), gdn.GDN_ERR_INVALID_ARG),
+    (dict(n=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(state=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(out=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dt=3), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dk=100, dv=100), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=64), gdn.GDN_ERR_UNSUPPORTED),
+])
+def test_decode_rejects(lib, over, status):
+    assert _decode(lib, **over) == status
+
+
+def test_decode_with_no_sequences_is_a_no_op(lib):
+    assert _decode(lib, n=0) == gdn.GDN_OK
+
+
+def test_python_binding_raises_on_bad_dtype():
+    import torch
+    q = torch.zeros(4, 2, 128, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        gdn.gdn_prefill(q, q, q, q, q)

@@ -1,0 +1,225 @@
+"""GPU path against the fp64 oracle on identical seeded inputs.
+
+Tolerances are the layer's parity bar: relative L2 <= 1e-2 for bf16 inputs
+and <= 1e-4 in the fp32-input mode, for outputs and final states, over the
+whole tensor; the worst (sequence, V head) slice is checked too so that an
+error confined to one short sequence cannot hide in the global norm.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import inputs as I
+from tests.gpu_util import log, per_seq_head_rel, per_state_rel, rel_l2, run_prefill, to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 1e-2
+TOL_FP32 = 1e-4
+TOL_BF16_SLICE = 2e-2   # worst single (sequence, head) slice; the bar itself is on the whole tensor
+
+
+def _oracle(x, heads=None):
+    return oracle.recurrent(x.q, x.k, x.v, x.g, x.beta, x.s0, x.cu_seqlens, scale=x.scale, heads=heads)
+
+
+def _check(x, out, fin, tol, slice_tol=None, heads=None):
+    ref_o, ref_f = _oracle(x, heads)
+    if heads is not None:
+        out = out[:, heads[0]:heads[1]]
+        fin = fin[:, heads[0]:heads[1]]
+    eo, ef = rel_l2(out, ref_o), rel_l2(fin, ref_f)
+    so = per_seq_head_rel(out, ref_o, x.cu_seqlens)
+    sf = per_state_rel(fin, ref_f)
+    log(f"[parity] {x.name}: out rel={eo:.3e} (worst slice {so:.3e})  state rel={ef:.3e} (worst {sf:.3e})")
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(fin))
+    assert eo <= tol and ef <= tol
+    st = tol if slice_tol is None else slice_tol
+    assert so <= st and sf <= st
+
+
+# ---------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("dtype,d,n", [("bf16", 128, 256), ("fp32", 128, 7), ("fp32", 64, 5),
+                                       ("fp32", 32, 3), ("fp32", 16, 9), ("bf16", 16, 4)])
+def test_decode_step(dtype, d, n):
+    x = I.draw(lengths=[1] * n, hqk=16 if d == 128 else 2, hv=32 if d == 128 else 4, dk=d, dtype=dtype,
+               seed=1003 if n == 256 else 50 + d, s0_std=0.01 if n == 256 else 0.3,
+               name=f"decode_{dtype}_d{d}_N{n}")
+    dev = to_device(x)
+    state = dev["s0"].clone()
+    log(f"[gpu] gdn_decode_step {x.name}")
+    import linear_attention_sequence_02_amd as gdn
+    out = gdn.gdn_decode_step(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], state, scale=x.scale)
+    torch.cuda.synchronize()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_FP32
+    _check(x, out.float().cpu().numpy().astype(np.float64), state.cpu().numpy().astype(np.float64), tol)
+
+
+# ---------------------------------------------------------------- fp32-input prefill
+
+def test_prefill_fp32_tiny():
+    x = I.tiny()
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_FP32)
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_prefill_fp32_varlen_shapes(d):
+    x = I.draw(lengths=[1, 63, 64, 65, 0, 130, 200], hqk=2, hv=4, dk=d, dtype="fp32", seed=60 + d,
+               s0_std=0.3, name=f"fp32_varlen_d{d}")
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_FP32)
+
+
+def test_prefill_fp32_qwen_shape():
+    x = I.qwen3_next_prefill(T=1000, dtype="fp32", seed=71)
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_FP32)
+
+
+# ---------------------------------------------------------------- bf16 MFMA prefill
+
+def test_prefill_bf16_small_varlen():
+    x = I.draw(lengths=[1, 63, 64, 65, 0, 200, 17, 128], hqk=2, hv=4, dk=128, dtype="bf16", seed=80,
+               s0_std=0.3, name="bf16_small_varlen")
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
+
+
+def test_prefill_bf16_qwen_layer_T4096():
+    x = I.qwen3_next_prefill(T=4096)
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
+
+
+def test_prefill_bf16_varlen8():
+    x = I.varlen_prefill()
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
+
+
+def test_prefill_bf16_long_context_sampled_heads():
+    # T = 262144 in the launch configuration of the full layer; the oracle
+    # recomputes one QK head's two V heads (heads are independent).
+    x = I.long_context()
+    log(f"[case] long context mean alpha={x.meta['mean_alpha']:.4f}")
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE, heads=(6, 8))
+
+
+def test_prefill_bf16_scale_argument():
+    x = I.draw(lengths=[300], hqk=2, hv=4, dk=128, dtype="bf16", seed=81, s0_std=0.1,
+               scale=1.0 / math.sqrt(128.0), name="bf16_scale")
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
+
+
+# Carry-sensitive cases: with the default decay (mean alpha 0.5) the state
+# forgets a chunk within a few tokens, so a broken carry between chunks or a
+# wrong initial state could still pass; these keep the carry alive.
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_prefill_long_carry_no_decay(dtype):
+    x = I.draw(lengths=[1000, 517], hqk=2, hv=4, dk=128, dtype=dtype, seed=82, s0_std=0.5,
+               fixed_g=0.0, fixed_beta=0.05, name=f"{dtype}_no_decay_small_beta")
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_BF16 if dtype == "bf16" else TOL_FP32, TOL_BF16_SLICE if dtype == "bf16" else None)
+
+
+def test_prefill_bf16_pure_decay_closed_form():
+    # beta = 0: o_t = exp(sum_{s<=t} g_s) S0 q_t, S_T = exp(sum g) S0 (no oracle involved).
+    x = I.draw(lengths=[333], hqk=1, hv=2, dk=128, dtype="bf16", seed=83, s0_std=1.0, g_mean=-6.0,
+               fixed_beta=0.0, name="bf16_pure_decay")
+    out, fin = run_prefill(x)
+    qf = I.bf16_bits_to_f32(x.q).astype(np.float64)
+    decay = np.exp(np.cumsum(x.g.astype(np.float64), axis=0))
+    s0 = x.s0.astype(np.float64)
+    exp_out = np.stack([decay[:, h, None] * (qf[:, 0] @ s0[0, h].T) for h in range(2)], axis=1)
+    exp_fin = decay[-1][None, :, None, None] * s0
+    log(f"[parity] pure decay: out {rel_l2(out, exp_out):.3e} state {rel_l2(fin, exp_fin):.3e}")
+    assert rel_l2(out, exp_out) <= TOL_BF16 and rel_l2(fin, exp_fin) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_prefill_resume_split(dtype):
+    # [0, T) in one call equals [0, T1) then [T1, T) from the saved state, T1 not a multiple of 64.
+    x = I.draw(lengths=[900], hqk=2, hv=4, dk=128, dtype=dtype, seed=84, s0_std=0.2, g_mean=-3.0,
+               name=f"{dtype}_resume")
+    out, fin = run_prefill(x)
+    T1 = 397
+    xa = I.GdnInputs(q=x.q[:T1], k=x.k[:T1], v=x.v[:T1], g=x.g[:T1], beta=x.beta[:T1], s0=x.s0,
+                     cu_seqlens=np.array([0, T1], np.int32), dtype=dtype, scale=1.0, name="resume_a",
+                     seed=0, meta={})
+    oa, fa = run_prefill(xa)
+    xb = I.GdnInputs(q=x.q[T1:], k=x.k[T1:], v=x.v[T1:], g=x.g[T1:], beta=x.beta[T1:],
+                     s0=fa.astype(np.float32), cu_seqlens=np.array([0, 900 - T1], np.int32), dtype=dtype,
+                     scale=1.0, name="resume_b", seed=0, meta={})
+    ob, fb = run_prefill(xb)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_FP32
+    ref_o, ref_f = _oracle(x)
+    split_o = np.concatenate([oa, ob])
+    log(f"[parity] resume {dtype}: split vs oracle out {rel_l2(split_o, ref_o):.3e} state {rel_l2(fb, ref_f):.3e}")
+    assert rel_l2(split_o, ref_o) <= tol and rel_l2(fb, ref_f) <= tol
+    assert rel_l2(split_o, out) <= tol and rel_l2(fb, fin) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_decode_steps_equal_prefill(dtype):
+    import linear_attention_sequence_02_amd as gdn
+    T = 12
+    x = I.draw(lengths=[T], hqk=2, hv=4, dk=128, dtype=dtype, seed=85, s0_std=0.3, g_mean=-2.0,
+               name=f"{dtype}_decode_chain")
+    d = to_device(x)
+    state = d["s0"].clone()
+    outs = []
+    log(f"[gpu] {T} chained decode steps {dtype}")
+    for t in range(T):
+        o = gdn.gdn_decode_step(d["q"][t:t + 1], d["k"][t:t + 1], d["v"][t:t + 1], d["g"][t:t + 1],
+                                d["beta"][t:t + 1], state)
+        outs.append(o.float().cpu().numpy().astype(np.float64))
+    torch.cuda.synchronize()
+    ref_o, ref_f = _oracle(x)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_FP32
+    assert rel_l2(np.concatenate(outs), ref_o) <= tol
+    assert rel_l2(state.cpu().numpy(), ref_f) <= tol
+
+
+def test_prefill_final_state_aliases_initial_state():
+    import linear_attention_sequence_02_amd as gdn
+    x = I.draw(lengths=[100, 0, 70], hqk=2, hv=4, dk=128, dtype="bf16", seed=86, s0_std=0.2,
+               name="bf16_alias")
+    d = to_device(x)
+    st = d["s0"].clone()
+    log("[gpu] prefill with final_state == initial_state")
+    out, fin = gdn.gdn_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], st, d["cu"], final_state=st)
+    torch.cuda.synchronize()
+    assert fin.data_ptr() == st.data_ptr()
+    ref_o, ref_f = _oracle(x)
+    assert rel_l2(out.float().cpu().numpy(), ref_o) <= TOL_BF16
+    assert rel_l2(st.cpu().numpy(), ref_f) <= TOL_BF16
+    assert np.array_equal(st[1].cpu().numpy(), x.s0[1])   # the empty sequence keeps its state exactly
+
+
+def test_prefill_no_tokens_copies_states():
+    import linear_attention_sequence_02_amd as gdn
+    dev = "cuda"
+    s0 = torch.randn(3, 4, 128, 128, device=dev)
+    cu = torch.zeros(4, dtype=torch.int32, device=dev)
+    e = torch.empty(0, 2, 128, dtype=torch.bfloat16, device=dev)
+    ev = torch.empty(0, 4, 128, dtype=torch.bfloat16, device=dev)
+    eg = torch.empty(0, 4, dtype=torch.float32, device=dev)
+    log("[gpu] prefill with zero tokens")
+    out, fin = gdn.gdn_prefill(e, e, ev, eg, eg, s0, cu)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 4, 128) and torch.equal(fin, s0)
+
+
+def test_prefill_deterministic():
+    x = I.draw(lengths=[500, 300], hqk=2, hv=4, dk=128, dtype="bf16", seed=87, s0_std=0.1, name="bf16_det")
+    o1, f1 = run_prefill(x)
+    o2, f2 = run_prefill(x)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
