@@ -1,0 +1,204 @@
+"""Benchmark of the Gated DeltaNet token mixer on one MI355X.
+
+One step = one gdn_prefill call over the Qwen3-Next GDN layer at T = 65536
+(B = 1, 16 QK / 32 V heads, d = 128, bf16 q/k/v, fp32 g/beta/state, chunk 64)
+with every input resident in HBM. The decode step (256 sequences x 32 heads,
+512 MiB fp32 state updated in place) is timed separately and reported under
+"decode". Per-kernel durations come from the library's HIP-event
+instrumentation over the timed region, on the stream the kernels run on.
+
+Roofline figures use algorithmic work only:
+  prefill, whole path: 4,194,304 flop and 24,832 bytes per token
+  prefill chain kernel: 3,670,016 flop per token (the S-dependent products and
+      the two chunk-local products per V head that feed and read U)
+  decode: 1,080,098,816 bytes per step for 256 sequences (state read + write
+      plus q, k, v, g, beta, out)
+Peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8.0 TB/s.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/s at T=64K (16 QK/32 V heads, d=128); decode GB/s vs peak"
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+PREFILL_FLOP_PER_TOKEN = 4_194_304
+PREFILL_BYTES_PER_TOKEN = 24_832
+CHAIN_FLOP_PER_TOKEN = 3_670_016
+PREP_FLOP_PER_TOKEN = PREFILL_FLOP_PER_TOKEN - CHAIN_FLOP_PER_TOKEN
+
+
+def decode_bytes(n, hqk=16, hv=32, d=128):
+    state = n * hv * d * d * 4 * 2
+    other = n * (2 * hqk * d * 2 + hv * d * 2 + hv * d * 2 + hv * 4 * 2)
+    return state + other
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_calls(fn, steps, warmup, torch, profile=True):
+    import linear_attention_sequence_02_amd as gdn
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if profile:
+        gdn.gdn_profile_start()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    kernels = gdn.gdn_profile_stop() if profile else {}
+    return start.elapsed_time(stop) / steps, {k: (c, ms / c) for k, (c, ms) in kernels.items()}
+
+
+def to_device(x, dev):
+    import torch
+    if x.dtype == "bf16":
+        def qkv(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
+    else:
+        def qkv(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    return dict(q=qkv(x.q), k=qkv(x.k), v=qkv(x.v), g=torch.from_numpy(x.g).to(dev),
+                beta=torch.from_numpy(x.beta).to(dev),
+                s0=None if x.s0 is None else torch.from_numpy(x.s0).to(dev),
+                cu=torch.from_numpy(x.cu_seqlens).to(dev))
+
+
+def cpu_baseline(x, budget_s=20.0):
+    """The fp64 oracle, as it is, on the host cores: a prefix of the same
+    workload (all 32 heads), grown until it takes a few seconds, scaled to tokens/s."""
+    import oracle
+    T = 512
+    while True:
+        t0 = time.perf_counter()
+        _, _, threads = oracle.recurrent(x.q[:T], x.k[:T], x.v[:T], x.g[:T], x.beta[:T], None, None,
+                                         scale=x.scale, return_threads=True)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or T >= x.T:
+            break
+        T = min(x.T, int(T * max(2.0, budget_s / 4 / max(dt, 1e-3))))
+    return {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {T} of {x.T} tokens of the same input, all {x.hv} V heads, fp64 recurrence, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--T", type=int, default=65536)
+    ap.add_argument("--decode-seqs", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the Gated DeltaNet layer "
+              "shards by heads or sequences with no exchange inside the mixer, so this build times the "
+              "one-GPU share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_attention_sequence_02_amd as gdn
+    from synth import inputs as I
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating T={args.T} inputs")
+    x = I.qwen3_next_prefill(T=args.T)
+    d = to_device(x, dev)
+    out = torch.empty_like(d["v"])
+    fin = torch.empty((1, x.hv, x.dv, x.dk), dtype=torch.float32, device=dev)
+    ws_bytes = gdn.gdn_prefill_workspace_size(x.T, 1, x.hqk, x.hv, x.dk, x.dv, gdn.GDN_BF16)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+
+    def prefill():
+        gdn.gdn_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, None, out=out, final_state=fin,
+                        workspace=ws)
+
+    log(f"[bench] prefill: {args.warmup} warmup + {args.steps} timed steps")
+    ms, kern = time_calls(prefill, args.steps, args.warmup, torch)
+    tokens_per_s = x.T / (ms / 1e3)
+    chain_ms = kern.get("gdn_chunk_chain", (0, float("nan")))[1]
+    prep_ms = kern.get("gdn_chunk_prep", (0, float("nan")))[1]
+    chain_tflops = CHAIN_FLOP_PER_TOKEN * x.T / (chain_ms / 1e3) / 1e12
+    path_tflops = PREFILL_FLOP_PER_TOKEN * x.T / (ms / 1e3) / 1e12
+    path_gbs = PREFILL_BYTES_PER_TOKEN * x.T / (ms / 1e3) / 1e9
+    log(f"[bench] prefill {ms:.3f} ms/step, {tokens_per_s:.3e} tokens/s; kernels {kern}")
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"qwen3next_gdn_prefill_T{x.T}", "batch": 1, "seq_len": x.T,
+                   "num_qk_heads": x.hqk, "num_v_heads": x.hv, "head_dim": x.dk, "chunk": 64,
+                   "seed": x.seed, "initial_state": "zeros"},
+        "roofline": {"kernel": "gdn_chunk_chain", "bound": "mfma", "achieved": chain_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": chain_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None, "ms_per_launch": chain_ms},
+        "prefill_path": {"tflops_algorithmic": path_tflops, "frac_mfma_peak": path_tflops / PEAK_BF16_TFLOPS,
+                         "gbs_algorithmic": path_gbs, "frac_hbm_peak": path_gbs / PEAK_HBM_GBS,
+                         "kernels_ms_per_launch": {k: v[1] for k, v in kern.items()}},
+    }
+    del d, out, fin, ws
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        n = args.decode_seqs
+        log(f"[bench] decode: {n} sequences")
+        y = I.decode_batch(n)
+        dd = to_device(y, dev)
+        state = dd["s0"].clone()
+        dout = torch.empty_like(dd["v"])
+
+        def decode():
+            gdn.gdn_decode_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], state, out=dout)
+
+        dms, dkern = time_calls(decode, args.steps, args.warmup, torch)
+        kms = dkern.get("gdn_decode_step", (0, dms))[1]
+        nbytes = decode_bytes(n)
+        gbs = nbytes / (kms / 1e3) / 1e9
+        result["decode"] = {"workload": f"qwen3next_gdn_decode_N{n}", "ms_per_step": dms,
+                            "kernel_ms_per_launch": kms, "bytes_per_step": nbytes, "GB_per_s": gbs,
+                            "frac_hbm_peak": gbs / PEAK_HBM_GBS, "tokens_per_s": n / (dms / 1e3),
+                            "roofline": {"kernel": "gdn_decode_step", "bound": "hbm", "achieved": gbs,
+                                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                         "traffic": None}}
+        log(f"[bench] decode {dms:.3f} ms/step, {gbs:.1f} GB/s")
+        del dd, state, dout
+
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle on host cores)")
+        result["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -121,6 +121,19 @@ gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v,
                              int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype,
                              void* out, void* stream);
 
+/*
+ * Instrumentation (for benchmarks and profiling; process-global, not
+ * thread-safe, not for graph capture). After gdn_profile_start(), every kernel
+ * the library launches is bracketed by a pair of HIP events recorded on the
+ * stream it is launched on. gdn_profile_stop() turns this off, waits for the
+ * recorded events and aggregates them per kernel: names receives up to
+ * max_kernels NUL-terminated names of at most 63 characters in slots of 64
+ * bytes, counts the launches and total_ms the summed durations. Returns the
+ * number of distinct kernels, or -1 if a HIP event call failed.
+ */
+gdn_status_t gdn_profile_start(void);
+int32_t gdn_profile_stop(int32_t max_kernels, char* names, int32_t* counts, double* total_ms);
+
 /* Static, NUL-terminated description of a status code. */
 const char* gdn_status_string(gdn_status_t status);
 

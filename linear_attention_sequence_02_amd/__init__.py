@@ -15,7 +15,7 @@ import threading
 import torch
 
 __all__ = ["gdn_prefill", "gdn_decode_step", "gdn_prefill_workspace_size", "gdn_status_string",
-           "gdn_build_info", "GDN_BF16", "GDN_FP32", "GdnError", "library_path"]
+           "gdn_build_info", "gdn_profile_start", "gdn_profile_stop", "GDN_BF16", "GDN_FP32", "GdnError", "library_path"]
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(5)
 GDN_BF16, GDN_FP32 = 0, 1
@@ -53,6 +53,11 @@ def _load():
             lib.gdn_status_string.argtypes = [ctypes.c_int]
             lib.gdn_build_info.restype = ctypes.c_char_p
             lib.gdn_build_info.argtypes = []
+            lib.gdn_profile_start.restype = ctypes.c_int
+            lib.gdn_profile_start.argtypes = []
+            lib.gdn_profile_stop.restype = ctypes.c_int32
+            lib.gdn_profile_stop.argtypes = [_i32, ctypes.c_char_p, ctypes.POINTER(_i32),
+                                             ctypes.POINTER(ctypes.c_double)]
             _lib = lib
     return _lib
 
@@ -63,6 +68,27 @@ def gdn_status_string(status: int) -> str:
 
 def gdn_build_info() -> str:
     return _load().gdn_build_info().decode()
+
+
+def gdn_profile_start() -> None:
+    """Start per-kernel event timing of every library launch (see include/gdn.h)."""
+    _load().gdn_profile_start()
+
+
+def gdn_profile_stop(max_kernels: int = 16) -> dict:
+    """Stop timing; returns {kernel name: (launch count, total milliseconds)}."""
+    names = ctypes.create_string_buffer(64 * max_kernels)
+    counts = (_i32 * max_kernels)()
+    totals = (ctypes.c_double * max_kernels)()
+    n = _load().gdn_profile_stop(max_kernels, names, counts, totals)
+    if n < 0:
+        raise RuntimeError("gdn_profile_stop: a HIP event call failed")
+    raw = names.raw
+    res = {}
+    for j in range(n):
+        name = raw[64 * j:64 * j + 64].split(b"\0", 1)[0].decode()
+        res[name] = (int(counts[j]), float(totals[j]))
+    return res
 
 
 def _dtype_code(t: torch.Tensor) -> int:

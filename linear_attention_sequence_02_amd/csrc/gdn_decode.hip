@@ -128,8 +128,10 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     constexpr int L = D / 16;
     constexpr int NT = (D * L < 256) ? D * L : 256;
     const int64_t blocks = (int64_t)a.num_seqs * a.num_v_heads;
+    prof::begin(stream, "gdn_decode_step");
     hipLaunchKernelGGL((decode_step_kernel<D, BF16>), dim3((unsigned)blocks), dim3(NT), 0, stream,
                        a.q, a.k, a.v, a.g, a.beta, a.state, a.num_qk_heads, a.num_v_heads, a.scale, a.out);
+    prof::end(stream);
     return hipGetLastError();
 }
 

@@ -40,6 +40,12 @@ struct PrefillArgs {
     bool bf16;
 };
 
+namespace prof {
+// Event pair around one kernel launch when instrumentation is on (no-op otherwise).
+void begin(hipStream_t s, const char* name);
+void end(hipStream_t s);
+}  // namespace prof
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);

@@ -471,14 +471,17 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const int64_t slots = a.total_tokens / kChunk + a.num_seqs;
     uint8_t* ws = static_cast<uint8_t*>(a.workspace);
     if (a.total_tokens > 0) {
+        prof::begin(stream, "gdn_chunk_prep");
         hipLaunchKernelGGL(prep_kernel, dim3((unsigned)slots, (unsigned)a.num_qk_heads), dim3(256), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, a.g, a.beta, a.cu_seqlens, a.num_seqs,
                            a.total_tokens, a.num_qk_heads, a.num_v_heads, ws);
+        prof::end(stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     // Fewer than ~2 workgroups per CU with whole heads: split the value columns in two.
     const int64_t units = (int64_t)a.num_seqs * a.num_v_heads;
+    prof::begin(stream, "gdn_chunk_chain");
     if (units >= 512) {
         hipLaunchKernelGGL((chain_kernel<2>), dim3((unsigned)units), dim3(256), 0, stream,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.beta,
@@ -490,6 +493,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
                            a.initial_state, a.cu_seqlens, a.final_state, (uint16_t*)a.out, ws, a.total_tokens,
                            a.num_qk_heads, a.num_v_heads, a.scale);
     }
+    prof::end(stream);
     return hipGetLastError();
 }
 

@@ -174,10 +174,12 @@ __global__ __launch_bounds__(2 * D) void prefill_f32_kernel(
 template <int D>
 static hipError_t launch_f32_t(const PrefillArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.num_seqs * a.num_v_heads;
+    prof::begin(stream, "gdn_prefill_f32");
     hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3((unsigned)blocks), dim3(2 * D), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, a.g, a.beta,
                        a.initial_state, a.cu_seqlens, a.final_state, (float*)a.out, a.total_tokens,
                        a.num_qk_heads, a.num_v_heads, a.scale);
+    prof::end(stream);
     return hipGetLastError();
 }
 

@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert set(declared_functions()) == {"gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step",
-                                         "gdn_status_string", "gdn_build_info"}
+                                         "gdn_status_string", "gdn_build_info", "gdn_profile_start",
+                                         "gdn_profile_stop"}
 
 
 def test_library_exports_every_declared_symbol(lib):
