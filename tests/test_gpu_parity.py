@@ -90,6 +90,14 @@ def test_prefill_bf16_small_varlen():
     _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
 
 
+def test_prefill_bf16_many_short_sequences():
+    # 24 sequences x 32 heads = 768 (sequence, head) pairs: the whole-head chain kernel.
+    lengths = [1, 5, 63, 64, 65, 0, 128, 300, 17, 200, 129, 2, 90, 64, 191, 40, 3, 77, 256, 1, 33, 100, 12, 70]
+    x = I.draw(lengths=lengths, hqk=16, hv=32, dk=128, dtype="bf16", seed=88, s0_std=0.1, name="bf16_many_short")
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
+
+
 def test_prefill_bf16_qwen_layer_T4096():
     x = I.qwen3_next_prefill(T=4096)
     out, fin = run_prefill(x)
