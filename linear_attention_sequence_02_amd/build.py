@@ -8,13 +8,15 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_prefill_f32.hip", "gdn_prefill_bf16.hip", "gdn_profile.hip"]
+SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_prefill_f32.hip", "gdn_segment.hip", "gdn_profile.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for every HIP file (the compiler would
 # otherwise pair ordinary float arithmetic into them).
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               # MFMA results in ordinary VGPRs (no accumulator-register copies on gfx950)
+               "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:
