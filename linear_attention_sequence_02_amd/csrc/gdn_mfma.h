@@ -67,6 +67,31 @@ __device__ __forceinline__ bf16x8 lds_row8(const uint16_t* tile, int ld, int row
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + row * ld + 32 * k + 8 * g));
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes, lane
+// i addresses 4 consecutive 16-bit values D[i][0..3]; lane j receives
+// D[4 e + j / 4][j % 4] for e = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+// A operand of K^T (row = key index 16 t + m, reduction = tokens) read from the
+// token-major K tile, in accumulator order: slots 0..3 are tokens
+// 32 kk + 4 g + 0..3 and slots 4..7 tokens 32 kk + 16 + 4 g + 0..3. Lane
+// (g, m) addresses row base + m / 4, columns 16 t + 4 (m % 4) .. + 3.
+__device__ __forceinline__ bf16x8 lds_kt_tr(const uint16_t* K, int ld, int t, int kk, int g, int m) {
+    const uint16_t* p = K + (32 * kk + 4 * g + (m >> 2)) * ld + 16 * t + 4 * (m & 3);
+    const i16x4 lo = lds_read_tr16(p);
+    const i16x4 hi = lds_read_tr16(p + 16 * ld);
+    u32x4 u;
+    u.x = __builtin_bit_cast(u32x2, lo).x;
+    u.y = __builtin_bit_cast(u32x2, lo).y;
+    u.z = __builtin_bit_cast(u32x2, hi).x;
+    u.w = __builtin_bit_cast(u32x2, hi).y;
+    return __builtin_bit_cast(bf16x8, u);
+}
+
 struct SeqRange {
     int64_t bos, eos;
 };

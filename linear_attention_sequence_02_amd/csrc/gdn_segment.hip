@@ -27,7 +27,9 @@
 // owns 32 value columns of the 128 x 128 state (two 16-column MFMA tiles,
 // fp32 accumulators held transposed: tile t, lane (g, m), element e is
 // S[col][key 16 t + 4 g + e]) and needs nothing from the other waves; the
-// factors of the chunk are built by all waves together in LDS.
+// factors of the chunk are built by all waves together in LDS. The state
+// update's K^T operand is read from the token-major K tile with the LDS
+// transpose read, so K is staged once.
 #include "gdn_mfma.h"
 
 namespace gdn {
@@ -60,7 +62,6 @@ __device__ __forceinline__ int find_seq_for_seg(const int32_t* cu, int N, int64_
 
 struct __attribute__((aligned(16))) SegSmem {
     uint16_t K[kChunk][RP];          // keys, token-major
-    uint16_t KT[D][CP];              // keys, key-index-major
     uint16_t Q[kChunk][RP];          // queries (output pass)
     uint16_t V[kChunk][RP];          // values
     uint16_t T[kChunk][CP];          // Tm, bf16
@@ -87,13 +88,11 @@ __device__ __forceinline__ void seg_fetch(SegPrefetch<NT>& pf, const uint16_t* k
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
         const int p = tid + NT * i;
-        const int row = p >> 4, c8 = p & 15;                 // row-major pieces (Q, V)
+        const int row = p >> 4, c8 = p & 15;                 // row-major 16-byte pieces
         const int rr = row < nc ? row : nc - 1;
         if (MODE == kModeOut) pf.q[i] = *reinterpret_cast<const u32x4*>(qc + rr * ldk + c8 * 8);
         pf.v[i] = *reinterpret_cast<const u32x4*>(vc + rr * ldv + c8 * 8);
-        const int krow = p & 63, kc8 = p >> 6;               // token-running pieces (K and its transpose)
-        const int kr = krow < nc ? krow : nc - 1;
-        pf.k[i] = *reinterpret_cast<const u32x4*>(kc + kr * ldk + kc8 * 8);
+        pf.k[i] = *reinterpret_cast<const u32x4*>(kc + rr * ldk + c8 * 8);
     }
     const int r = tid & 63;
     const float* sp = (tid < 64) ? gc : bc;
@@ -108,7 +107,7 @@ __device__ __forceinline__ void seg_stage(SegSmem& sm, SegPrefetch<NT>& pf, int 
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
             const int p = tid + NT * i;
-            pf.k[i] = (p & 63) < nc ? pf.k[i] : z;
+            pf.k[i] = (p >> 4) < nc ? pf.k[i] : z;
             pf.q[i] = (p >> 4) < nc ? pf.q[i] : z;
             pf.v[i] = (p >> 4) < nc ? pf.v[i] : z;
         }
@@ -118,11 +117,7 @@ __device__ __forceinline__ void seg_stage(SegSmem& sm, SegPrefetch<NT>& pf, int 
     for (int i = 0; i < NP; ++i) {
         const int p = tid + NT * i;
         const int row = p >> 4, c8 = p & 15;
-        const int krow = p & 63, kc8 = p >> 6;
-        *reinterpret_cast<u32x4*>(&sm.K[krow][kc8 * 8]) = pf.k[i];
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            sm.KT[kc8 * 8 + s][krow] = (uint16_t)((s & 1) ? (pf.k[i][s >> 1] >> 16) : (pf.k[i][s >> 1] & 0xFFFFu));
+        *reinterpret_cast<u32x4*>(&sm.K[row][c8 * 8]) = pf.k[i];
         if (MODE == kModeOut) *reinterpret_cast<u32x4*>(&sm.Q[row][c8 * 8]) = pf.q[i];
         *reinterpret_cast<u32x4*>(&sm.V[row][c8 * 8]) = pf.v[i];
     }
@@ -334,8 +329,8 @@ __device__ __forceinline__ void seg_chain(SegSmem& sm, f32x4 (&ST)[8][2], int cw
     const float Glast = sm.Gam[kChunk - 1];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const bf16x8 a0 = lds_a_perm(&sm.KT[0][0], CP, 16 * t + m, 0, g);
-        const bf16x8 a1 = lds_a_perm(&sm.KT[0][0], CP, 16 * t + m, 1, g);
+        const bf16x8 a0 = lds_kt_tr(&sm.K[0][0], RP, t, 0, g, m);
+        const bf16x8 a1 = lds_kt_tr(&sm.K[0][0], RP, t, 1, g, m);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             f32x4 acc = ST[t][nt] * Glast;
