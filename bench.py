@@ -8,12 +8,16 @@ with every input resident in HBM. The decode step (256 sequences x 32 heads,
 instrumentation over the timed region, on the stream the kernels run on.
 
 Roofline figures use algorithmic work only:
-  prefill, whole path: 4,194,304 flop and 24,832 bytes per token
-  prefill chain kernel: 3,670,016 flop per token (the S-dependent products and
-      the two chunk-local products per V head that feed and read U)
+  prefill: 4,194,304 flop and 24,832 bytes per token (the output pass, the
+      dominant kernel, performs this whole per-token algorithm; the segment-map
+      pass and the combine are extra work of the segment-parallel schedule)
   decode: 1,080,098,816 bytes per step for 256 sequences (state read + write
       plus q, k, v, g, beta, out)
 Peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8.0 TB/s.
+HBM traffic per launch ("traffic") comes from rocprofv3 FETCH_SIZE and
+WRITE_SIZE passes recorded in profiles/traffic.json, scaled by the same
+counters read for a plain device copy of known size (--calibration-copy); it
+is reported only while the kernel source matches the recorded hash.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -36,8 +40,9 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 PREFILL_FLOP_PER_TOKEN = 4_194_304
 PREFILL_BYTES_PER_TOKEN = 24_832
-CHAIN_FLOP_PER_TOKEN = 3_670_016
-PREP_FLOP_PER_TOKEN = PREFILL_FLOP_PER_TOKEN - CHAIN_FLOP_PER_TOKEN
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {"gdn_segment_out": "gdn_segment.hip", "gdn_segment_maps": "gdn_segment.hip",
+                  "gdn_decode_step": "gdn_decode.hip"}
 
 
 def decode_bytes(n, hqk=16, hv=32, d=128):
@@ -66,6 +71,30 @@ def time_calls(fn, steps, warmup, torch, profile=True):
     torch.cuda.synchronize()
     kernels = gdn.gdn_profile_stop() if profile else {}
     return start.elapsed_time(stop) / steps, {k: (c, ms / c) for k, (c, ms) in kernels.items()}
+
+
+def source_hash(kernel):
+    import hashlib
+    src = KERNEL_SOURCES.get(kernel)
+    if src is None:
+        return None
+    h = hashlib.sha256()
+    for f in (src, "gdn_mfma.h", "gdn_common.h"):
+        path = os.path.join(ROOT, "linear_attention_sequence_02_amd", "csrc", f)
+        if os.path.exists(path):
+            h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch measured with rocprofv3 for this kernel source, or None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE)).get(f"{kernel}@{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def to_device(x, dev):
@@ -109,6 +138,8 @@ def main():
     ap.add_argument("--decode-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run one 256 MiB device-to-device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the Gated DeltaNet layer "
@@ -137,11 +168,12 @@ def main():
     log(f"[bench] prefill: {args.warmup} warmup + {args.steps} timed steps")
     ms, kern = time_calls(prefill, args.steps, args.warmup, torch)
     tokens_per_s = x.T / (ms / 1e3)
-    chain_ms = kern.get("gdn_chunk_chain", (0, float("nan")))[1]
-    prep_ms = kern.get("gdn_chunk_prep", (0, float("nan")))[1]
-    chain_tflops = CHAIN_FLOP_PER_TOKEN * x.T / (chain_ms / 1e3) / 1e12
+    dom = max(kern, key=lambda k_: kern[k_][0] * kern[k_][1]) if kern else None
+    dom_ms = kern[dom][1] if dom else float("nan")
+    dom_tflops = PREFILL_FLOP_PER_TOKEN * x.T / (dom_ms / 1e3) / 1e12
     path_tflops = PREFILL_FLOP_PER_TOKEN * x.T / (ms / 1e3) / 1e12
     path_gbs = PREFILL_BYTES_PER_TOKEN * x.T / (ms / 1e3) / 1e9
+    workload = f"qwen3next_gdn_prefill_T{x.T}"
     log(f"[bench] prefill {ms:.3f} ms/step, {tokens_per_s:.3e} tokens/s; kernels {kern}")
 
     result = {
@@ -157,15 +189,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"qwen3next_gdn_prefill_T{x.T}", "batch": 1, "seq_len": x.T,
+        "config": {"workload": workload, "batch": 1, "seq_len": x.T,
                    "num_qk_heads": x.hqk, "num_v_heads": x.hv, "head_dim": x.dk, "chunk": 64,
                    "seed": x.seed, "initial_state": "zeros"},
-        "roofline": {"kernel": "gdn_chunk_chain", "bound": "mfma", "achieved": chain_tflops,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": chain_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None, "ms_per_launch": chain_ms},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": dom_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": recorded_traffic(dom, workload), "ms_per_launch": dom_ms},
         "prefill_path": {"tflops_algorithmic": path_tflops, "frac_mfma_peak": path_tflops / PEAK_BF16_TFLOPS,
                          "gbs_algorithmic": path_gbs, "frac_hbm_peak": path_gbs / PEAK_HBM_GBS,
-                         "kernels_ms_per_launch": {k: v[1] for k, v in kern.items()}},
+                         "kernels_ms_per_launch": {k_: v_[1] for k_, v_ in kern.items()}},
     }
     del d, out, fin, ws
     torch.cuda.empty_cache()
@@ -190,9 +222,18 @@ def main():
                             "frac_hbm_peak": gbs / PEAK_HBM_GBS, "tokens_per_s": n / (dms / 1e3),
                             "roofline": {"kernel": "gdn_decode_step", "bound": "hbm", "achieved": gbs,
                                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                                         "traffic": None}}
+                                         "traffic": recorded_traffic("gdn_decode_step", f"qwen3next_gdn_decode_N{n}")}}
         log(f"[bench] decode {dms:.3f} ms/step, {gbs:.1f} GB/s")
         del dd, state, dout
+
+    if args.calibration_copy:
+        a_ = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b_ = torch.empty_like(a_)
+        torch.cuda.synchronize()
+        b_.copy_(a_)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 268435456 bytes read, 268435456 bytes written")
+        del a_, b_
 
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle on host cores)")
