@@ -3,33 +3,35 @@
 // Chunk algebra (chunk of n <= 64 tokens, entry state S (d_v x d_k), gamma =
 // in-chunk cumulative sum of g, Gamma = exp(gamma)):
 //   A[r][c] = beta_r exp(gamma_r - gamma_c) (k_r . k_c)   c < r   decay-masked Gram
-//   Tm      = (I + A)^-1                                          UT transform
-//   U       = Tm (beta * (V - Gamma * (K S^T)))                   the chunk's delta writes
+//   U       solves (I + A) U = beta * (V - Gamma * (K S^T))       the chunk's delta writes
 //   O       = scale (Gamma * (Q S^T) + P U),  P[r][c] = exp(gamma_r - gamma_c) (q_r . k_c), c <= r
 //   S_end   = Gamma_last S + U^T diag(exp(gamma_last - gamma)) K
 // (unrolling the per-token rule inside the chunk: the write of token r sees
 // the decayed entry state plus the chunk's earlier writes, which is the unit
-// lower-triangular system (I + A) U = beta * (V - Gamma * K S^T)).
+// lower-triangular system above). The system is solved by 16-row blocks:
+// U_b = (I + A_bb)^-1 (X_b - sum_{b' < b} A_bb' U_b'), so only the four 16 x 16
+// diagonal blocks are inverted; the off-diagonal blocks are applied by MFMA.
 //
 // Segments. S_end is affine in the entry state: over a segment of L chunks,
 // S_end = S_in M_seg + H_seg, where H_seg is the segment run from S_in = 0 and
 // M_seg (d_k x d_k) the run from S_in = I with V = 0. The launches:
 //   pass A   every segment but a sequence's last: H (segment 0 starts from
 //            the sequence's initial state, so its H is its end state) and,
-//            for segments >= 1, M; one 8-wave workgroup computes both.
+//            for segments >= 1, M.
 //   combine  S_in(1) = H_0, S_in(j+1) = S_in(j) M_j + H_j, in fp32.
 //   pass C   every segment from its true entry state: outputs and, for the
 //            last segment, the final state.
-// Each chunk's factors (Gram products, masks, Tm, P) are computed inside the
-// workgroup that uses them, so nothing but the states leaves the chip.
 //
-// Work split. A workgroup is one (segment, V head). Every wave of a chain
-// owns 32 value columns of the 128 x 128 state (two 16-column MFMA tiles,
-// fp32 accumulators held transposed: tile t, lane (g, m), element e is
-// S[col][key 16 t + 4 g + e]) and needs nothing from the other waves; the
-// factors of the chunk are built by all waves together in LDS. The state
-// update's K^T operand is read from the token-major K tile with the LDS
-// transpose read, so K is staged once.
+// Work split inside a workgroup (one (segment, V head)):
+//   chain waves     each owns 32 value columns of a 128 x 128 fp32 state (pass
+//                   C: one state over 4 waves; pass A: H and M over 8 waves),
+//                   held in MFMA accumulators, and runs chunk c.
+//   producer waves  (4) meanwhile build chunk c + 1's factors (masked Gram
+//                   blocks, diagonal-block inverses, decay vectors) and stage
+//                   chunk c + 2's K (and Q) tiles from registers into LDS.
+// K/Q tiles are triple-buffered and the factors double-buffered, so one
+// workgroup barrier per chunk separates producers from consumers. Values and
+// outputs go straight between HBM and the chain waves' registers.
 #include "gdn_mfma.h"
 
 namespace gdn {
@@ -41,6 +43,14 @@ namespace {
 enum { kModeOut = 0, kModeHM = 1 };
 constexpr size_t kSegMat = (size_t)D * D;   // floats in one 128 x 128 matrix
 constexpr int kSegMats = 3;                 // H, M, S_in per (segment, V head)
+constexpr int kProd = 4;                    // producer waves per workgroup
+constexpr int TP = 20;                      // bf16 row pitch of the 16 x 16 factor blocks
+constexpr int AP = 20;                      // fp32 row pitch of a producer's diagonal A block
+
+template <int MODE>
+struct ChainWaves {
+    static constexpr int n = 4;
+};
 
 // Segments: sequence n owns [f(n), f(n) + nseg_n) with f(n) = cu[n] / (64 L) + n;
 // the ranges are disjoint and below total_tokens / (64 L) + num_seqs, so the
@@ -60,277 +70,344 @@ __device__ __forceinline__ int find_seq_for_seg(const int32_t* cu, int N, int64_
     return lo;
 }
 
+// One chunk's factors. Blocks are row-major 16 x 16 bf16 (row = the chunk's
+// token 16 b + r), read by the chain as 16x16x16 MFMA A operands.
+struct __attribute__((aligned(16))) ChunkFactors {
+    uint16_t Td[4][16][TP];     // (I + A_bb)^-1
+    uint16_t An[6][16][TP];     // -A_bb' for b > b', at b (b - 1) / 2 + b'
+    uint16_t P[10][16][TP];     // P blocks (mt >= nt), at mt (mt + 1) / 2 + nt (output pass)
+    float Gam[kChunk], Dec[kChunk], bet[kChunk];
+};
+
+template <int MODE>
 struct __attribute__((aligned(16))) SegSmem {
-    uint16_t K[kChunk][RP];          // keys, token-major
-    uint16_t Q[kChunk][RP];          // queries (output pass)
-    uint16_t V[kChunk][RP];          // values
-    uint16_t T[kChunk][CP];          // Tm, bf16
-    uint16_t P[kChunk][CP];          // P, bf16 (output pass)
-    float A[kChunk][kChunk + 1];     // A, fp32 (strictly lower part used)
-    float Tf[kChunk][kChunk + 1];    // Tm, fp32, during the solve
-    float gam[kChunk], Gam[kChunk], Dec[kChunk], bet[kChunk];
+    uint16_t K[3][kChunk][RP];                          // keys, token-major
+    uint16_t Q[(MODE == kModeOut) ? 3 : 1][kChunk][RP]; // queries (output pass)
+    ChunkFactors F[2];
+    float Ad[kProd][16][AP];                            // producer scratch: diagonal block of A
+    float pg[kProd][kChunk], pb[kProd][kChunk];         // producer scratch: gamma, beta
 };
 
-template <int NT>
-struct SegPrefetch {
-    static constexpr int NP = kChunk * (D / 8) / NT;   // 16-byte pieces per thread per 64 x 128 tile
-    u32x4 k[NP], q[NP], v[NP];
-    float s;                                           // g (wave 0) or beta (wave 1)
-};
-
-// Loads for one chunk of nc tokens. Rows past the end re-read row nc - 1 (they
-// are zeroed when stored), so no load leaves the sequence and none is branched.
-template <int MODE, int NT>
-__device__ __forceinline__ void seg_fetch(SegPrefetch<NT>& pf, const uint16_t* kc, const uint16_t* qc,
-                                          const uint16_t* vc, const float* gc, const float* bc, int nc, int ldk,
-                                          int ldv, int num_v_heads, int tid) {
-    constexpr int NP = SegPrefetch<NT>::NP;
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        const int p = tid + NT * i;
-        const int row = p >> 4, c8 = p & 15;                 // row-major 16-byte pieces
-        const int rr = row < nc ? row : nc - 1;
-        if (MODE == kModeOut) pf.q[i] = *reinterpret_cast<const u32x4*>(qc + rr * ldk + c8 * 8);
-        pf.v[i] = *reinterpret_cast<const u32x4*>(vc + rr * ldv + c8 * 8);
-        pf.k[i] = *reinterpret_cast<const u32x4*>(kc + rr * ldk + c8 * 8);
-    }
-    const int r = tid & 63;
-    const float* sp = (tid < 64) ? gc : bc;
-    pf.s = sp[(r < nc ? r : nc - 1) * num_v_heads];
+// Global access as wave-uniform base + 32-bit byte offset (the SGPR-base form
+// of global loads and stores: one address VGPR instead of two).
+template <class T>
+__device__ __forceinline__ T ld_at(const void* base, uint32_t byte_off) {
+    return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+template <class T>
+__device__ __forceinline__ void st_at(void* base, uint32_t byte_off, T x) {
+    *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off) = x;
 }
 
-template <int MODE, int NT>
-__device__ __forceinline__ void seg_stage(SegSmem& sm, SegPrefetch<NT>& pf, int nc, int tid, int w) {
-    constexpr int NP = SegPrefetch<NT>::NP;
+// Producer registers: K (and Q) 16-byte pieces of the chunk two ahead, and g,
+// beta (row = lane) of the chunk one ahead.
+struct ProdRegs {
+    u32x4 k[4], q[4];
+    float g, b;
+};
+
+// Rows past the end of a chunk re-read its last row (they are zeroed when
+// staged), so no load leaves the sequence and none is branched.
+// Piece i of producer lane pl: row 16 i + pl / 16, 16-byte column block pl % 16.
+template <int MODE>
+__device__ __forceinline__ void prod_fetch_kq(ProdRegs& pr, const uint16_t* kc, const uint16_t* qc, int nc, int ldk,
+                                              int pl) {
+    const int r0 = pl >> 4;
+    if (nc == kChunk) {
+        const uint32_t off = (uint32_t)(r0 * ldk + (pl & 15) * 8) * 2u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr.k[i] = ld_at<u32x4>(kc + 16 * i * ldk, off);
+            if (MODE == kModeOut) pr.q[i] = ld_at<u32x4>(qc + 16 * i * ldk, off);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = r0 + 16 * i;
+            const uint32_t off = (uint32_t)((row < nc ? row : nc - 1) * ldk + (pl & 15) * 8) * 2u;
+            pr.k[i] = ld_at<u32x4>(kc, off);
+            if (MODE == kModeOut) pr.q[i] = ld_at<u32x4>(qc, off);
+        }
+    }
+}
+
+__device__ __forceinline__ void prod_fetch_gb(ProdRegs& pr, const float* gc, const float* bc, int nc, int hv,
+                                              int lane) {
+    const uint32_t off = (uint32_t)((lane < nc ? lane : nc - 1) * hv) * 4u;
+    pr.g = ld_at<float>(gc, off);
+    pr.b = ld_at<float>(bc, off);
+}
+
+template <int MODE>
+__device__ __forceinline__ void prod_stage_kq(SegSmem<MODE>& sm, int buf, const ProdRegs& pr, int nc, int pl) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    if (nc < kChunk) {   // partial last chunk: rows past the end are zero (uniform branch)
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int p = tid + NT * i;
-            pf.k[i] = (p >> 4) < nc ? pf.k[i] : z;
-            pf.q[i] = (p >> 4) < nc ? pf.q[i] : z;
-            pf.v[i] = (p >> 4) < nc ? pf.v[i] : z;
-        }
-        pf.s = (tid & 63) < nc ? pf.s : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        const int p = tid + NT * i;
+    for (int i = 0; i < 4; ++i) {
+        const int p = pl + 256 * i;
         const int row = p >> 4, c8 = p & 15;
-        *reinterpret_cast<u32x4*>(&sm.K[row][c8 * 8]) = pf.k[i];
-        if (MODE == kModeOut) *reinterpret_cast<u32x4*>(&sm.Q[row][c8 * 8]) = pf.q[i];
-        *reinterpret_cast<u32x4*>(&sm.V[row][c8 * 8]) = pf.v[i];
-    }
-    const int lane = tid & 63;
-    if (w == 0) {
-        // gamma = in-chunk inclusive prefix sum of g (padded rows add 0)
-        float x = pf.s;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float y = __shfl_up(x, d, 64);
-            if (lane >= d) x += y;
-        }
-        const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
-        sm.gam[lane] = x;
-        sm.Gam[lane] = fast_exp(x);
-        sm.Dec[lane] = fast_exp(glast - x);
-    } else if (w == 1) {
-        sm.bet[lane] = pf.s;
+        const bool in = row < nc;
+        *reinterpret_cast<u32x4*>(&sm.K[buf][row][c8 * 8]) = in ? pr.k[i] : z;
+        if (MODE == kModeOut) *reinterpret_cast<u32x4*>(&sm.Q[buf][row][c8 * 8]) = in ? pr.q[i] : z;
     }
 }
 
-// fp32 MFMA 16x16x4: lane (g, m) supplies A[m][g] and B[g][m]; D[4 g + e][m] in element e.
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Off-diagonal 16 x 16 blocks of Tm at distance L from the diagonal, one block
-// per wave: Tm[bi][bj] = -Tm[bi][bi] X with X = A[bi rows][16 bj : 16 bi]
-// Tm[16 bj : 16 bi][bj cols], both products in fp32 MFMA. X stays in the
-// accumulators: the second product takes it as its B operand by visiting the
-// reduction index 4 g + kk in step kk (the A operand follows the same order).
-template <int L>
-__device__ __forceinline__ void tsolve_level(SegSmem& sm, int w, int g, int m) {
-    if (w < 4 - L) {
-        const int bj = w, bi = w + L;
-        f32x4 X = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4 * L; ++kk)
-            X = mfma_f32(sm.A[16 * bi + m][16 * bj + 4 * kk + g], sm.Tf[16 * bj + 4 * kk + g][16 * bj + m], X);
-        f32x4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) Y = mfma_f32(sm.Tf[16 * bi + m][16 * bi + 4 * g + kk], X[kk], Y);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.Tf[16 * bi + 4 * g + e][16 * bj + m] = -Y[e];
-    }
-    __syncthreads();
-}
-
-// The chunk's factors in LDS: A and P (masked Gram products by MFMA), then
-// Tm = (I + A)^-1 by forward substitution on the 16 x 16 diagonal blocks
-// (wave 0, lane = 16 b + column) and three levels of fp32 block products.
-template <int MODE, int NT>
-__device__ __forceinline__ void seg_prep(SegSmem& sm, int tid, int w, int lg, int lm) {
-    constexpr int NWAVE = NT / 64;
-    constexpr int NJOBS = (MODE == kModeOut) ? 20 : 10;
-    for (int job = w; job < NJOBS; job += NWAVE) {
-        const int which = job / 10, ti = job % 10;        // 0: K K^T -> A, 1: Q K^T -> P
-        const int mt = (ti >= 6) ? 3 : (ti >= 3) ? 2 : (ti >= 1) ? 1 : 0;
-        const int nt = ti - mt * (mt + 1) / 2;
-        const uint16_t* Asrc = which ? &sm.Q[0][0] : &sm.K[0][0];
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            acc = mfma16(lds_row8(Asrc, RP, 16 * mt + lm, kk, lg), lds_row8(&sm.K[0][0], RP, 16 * nt + lm, kk, lg), acc);
-        const int cc = 16 * nt + lm;
-        const float gc = sm.gam[cc];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * mt + 4 * lg + e;
-            const float dec = (cc <= r) ? fast_exp(sm.gam[r] - gc) : 0.f;
-            if (which) sm.P[r][cc] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dec * acc[e]));
-            else sm.A[r][cc] = (cc < r) ? sm.bet[r] * dec * acc[e] : 0.f;
-        }
-    }
-    __syncthreads();
-    if (w == 0) {
-        const int b = lg, col = lm;
-        float t[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float* arow = &sm.A[16 * b + r][16 * b];
-            float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < r; ++jj) {
-                const float term = arow[jj] * t[jj];
-                if ((jj & 3) == 0) p0 += term;
-                else if ((jj & 3) == 1) p1 += term;
-                else if ((jj & 3) == 2) p2 += term;
-                else p3 += term;
-            }
-            t[r] = (r == col ? 1.f : 0.f) - ((p0 + p1) + (p2 + p3));
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sm.Tf[16 * b + r][16 * b + col] = t[r];
-    }
-    __syncthreads();
-    tsolve_level<1>(sm, w, lg, lm);
-    tsolve_level<2>(sm, w, lg, lm);
-    tsolve_level<3>(sm, w, lg, lm);
-    // Tm (lower block triangle) to bf16; its upper blocks were zeroed once.
-    for (int e = tid; e < 10 * 128; e += NT) {
-        const int ti = e >> 7, ii = (e >> 3) & 15, c2 = e & 7;
-        const int mt = (ti >= 6) ? 3 : (ti >= 3) ? 2 : (ti >= 1) ? 1 : 0;
-        const int nt = ti - mt * (mt + 1) / 2;
-        const int r = 16 * mt + ii, c = 16 * nt + 2 * c2;
-        *reinterpret_cast<uint32_t*>(&sm.T[r][c]) = pack_bf16(sm.Tf[r][c], sm.Tf[r][c + 1]);
-    }
-    __syncthreads();
-}
-
-// One chunk of one chain for this wave's 32 value columns (cw .. cw + 31).
-// ST: S^T accumulator tiles. WITH_V: values present (false for the M map).
-template <bool WITH_V, bool WITH_OUT>
-__device__ __forceinline__ void seg_chain(SegSmem& sm, f32x4 (&ST)[8][2], int cw, int g, int m, uint16_t* orow0,
-                                          int ldv, int nc, float scale) {
-    bf16x8 Sb[4][2];
+// 16 x 16 Gram block: rows 16 mt .. of X times rows 16 nt .. of K, transposed;
+// lane (g, m) gets element [16 mt + 4 g + e][16 nt + m].
+__device__ __forceinline__ f32x4 gram_block(const uint16_t* X, const uint16_t* K, int mt, int nt, int g, int m) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
+        acc = mfma16(lds_row8(X, RP, 16 * mt + m, kk, g), lds_row8(K, RP, 16 * nt + m, kk, g), acc);
+    return acc;
+}
+
+__device__ __forceinline__ void store_block_bf16(uint16_t (*blk)[TP], const f32x4& v, int g, int m) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) Sb[kk][nt] = pack_acc_pair(ST[2 * kk][nt], ST[2 * kk + 1][nt]);
-    // beta R = beta (V - Gamma K S^T)
-    f32x4 BR[4][2];
+    for (int e = 0; e < 4; ++e) blk[4 * g + e][m] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[e]));
+}
+
+// Factors of one chunk (its K/Q tiles in buffer kb) into F: producer wave pw
+// owns diagonal block pw (Gram, mask, inverse) and jobs pw, pw + 4, ... of the
+// off-diagonal A blocks (jobs 0..5) and the P blocks (jobs 6..15).
+template <int MODE>
+__device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFactors& F, const ProdRegs& pr, int nc,
+                                             int pw, int lane) {
+    const uint16_t* K = &sm.K[kb][0][0];
+    const uint16_t* Q = &sm.Q[(MODE == kModeOut) ? kb : 0][0][0];
+    const int g = lane >> 4, m = lane & 15;
+
+    // gamma = in-chunk inclusive prefix sum of g; rows past nc add 0 and have beta 0.
+    float x = lane < nc ? pr.g : 0.f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    const float bt = lane < nc ? pr.b : 0.f;
+    sm.pg[pw][lane] = x;
+    sm.pb[pw][lane] = bt;
+    if (pw == 0) {
+        const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+        F.Gam[lane] = fast_exp(x);
+        F.Dec[lane] = fast_exp(glast - x);
+        F.bet[lane] = bt;
+    }
+
+    // Diagonal block pw of A, fp32, strictly lower.
+    {
+        const f32x4 acc = gram_block(K, K, pw, pw, g, m);
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[pw][16 * pw + 4 * g]);
+        const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[pw][16 * pw + 4 * g]);
+        const float gc = sm.pg[pw][16 * pw + m];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = br[e] * fast_exp(gr[e] - gc) * acc[e];
+            sm.Ad[pw][4 * g + e][m] = (m < 4 * g + e) ? a : 0.f;
+        }
+    }
+
+    // Off-diagonal A blocks (stored negated) and P blocks.
+    constexpr uint64_t kRow = 0x3333222110333221ull, kCol = 0x3210210100210100ull;
+    constexpr int NJOBS = (MODE == kModeOut) ? 16 : 6;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int job = pw + 4 * jj;
+        if (job < NJOBS) {
+            const int mt = (int)((kRow >> (4 * job)) & 15), nt = (int)((kCol >> (4 * job)) & 15);
+            const bool isP = job >= 6;
+            const f32x4 acc = gram_block(isP ? Q : K, K, mt, nt, g, m);
+            const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[pw][16 * mt + 4 * g]);
+            const float gc = sm.pg[pw][16 * nt + m];
+            f32x4 v;
+            if (isP) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p = fast_exp(gr[e] - gc) * acc[e];
+                    v[e] = (mt > nt || m <= 4 * g + e) ? p : 0.f;
+                }
+                store_block_bf16(F.P[job - 6], v, g, m);
+            } else {
+                const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[pw][16 * mt + 4 * g]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = -(br[e] * fast_exp(gr[e] - gc) * acc[e]);
+                store_block_bf16(F.An[job], v, g, m);
+            }
+        }
+    }
+
+    // (I + A_pw)^-1 by forward substitution: lane (g, m) computes column m
+    // (the four lane groups redundantly) and stores rows 4 g .. 4 g + 3.
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float p0 = (r == m) ? 1.f : 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+        for (int j = 0; j < r; ++j) {
+            const float term = sm.Ad[pw][r][j] * t[j];
+            if ((j & 3) == 0) p0 -= term;
+            else if ((j & 3) == 1) p1 -= term;
+            else if ((j & 3) == 2) p2 -= term;
+            else p3 -= term;
+        }
+        t[r] = (p0 + p1) + (p2 + p3);
+    }
+    f32x4 col;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) col[e] = g == 0 ? t[e] : g == 1 ? t[4 + e] : g == 2 ? t[8 + e] : t[12 + e];
+    store_block_bf16(F.Td[pw], col, g, m);
+}
+
+__device__ __forceinline__ i16x4 lds_blk_a(const uint16_t (*blk)[TP], int g, int m) {
+    return __builtin_bit_cast(i16x4, *reinterpret_cast<const u32x2*>(&blk[m][4 * g]));
+}
+
+__device__ __forceinline__ f32x4 mfma_x16(i16x4 a, i16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Accumulator tile -> 16x16x16 B operand (reduction index 4 g + e).
+__device__ __forceinline__ i16x4 pack4(const f32x4& v) {
+    u32x2 u;
+    u.x = pack_bf16(v[0], v[1]);
+    u.y = pack_bf16(v[2], v[3]);
+    return __builtin_bit_cast(i16x4, u);
+}
+
+// Chain-wave values: rows 16 mt + 4 g + e, columns cb + 2 m, cb + 2 m + 1 of
+// the chunk whose (row 0, column cb) element vc points at (wave-uniform).
+__device__ __forceinline__ void chain_fetch_v(uint32_t (&vr)[16], const uint16_t* vc, int nc, int ldv, int g, int m) {
+    if (nc == kChunk) {
+        const uint32_t off = (uint32_t)(4 * g * ldv + 2 * m) * 2u;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vr[4 * mt + e] = ld_at<uint32_t>(vc + (16 * mt + e) * ldv, off);
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * mt + 4 * g + e;
+                const uint32_t off = (uint32_t)((row < nc ? row : nc - 1) * ldv + 2 * m) * 2u;
+                vr[4 * mt + e] = ld_at<uint32_t>(vc, off);
+            }
+    }
+}
+
+// One chunk of one chain for this wave's 32 value columns; lane (g, m) holds
+// columns cb + 2 m (tile nt = 0) and cb + 2 m + 1 (nt = 1). ST[t][nt] element e
+// is S[column][key 16 t + 4 g + e]. vr holds this chunk's values on entry and
+// the next chunk's (from vnext) on return.
+template <bool WITH_V, bool WITH_OUT>
+__device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q, const ChunkFactors& F,
+                                           f32x4 (&ST)[8][2], uint32_t (&vr)[16], const uint16_t* vnext, int ncn,
+                                           uint16_t* orow0, int ldv, int nc, float scale, int g, int m) {
+    // Z = K S^T
+    f32x4 X[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) X[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 sb0 = pack_acc_pair(ST[2 * kk][0], ST[2 * kk + 1][0]);
+        const bf16x8 sb1 = pack_acc_pair(ST[2 * kk][1], ST[2 * kk + 1][1]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const bf16x8 a = lds_a_perm(K, RP, 16 * mt + m, kk, g);
+            X[mt][0] = mfma16(a, sb0, X[mt][0]);
+            X[mt][1] = mfma16(a, sb1, X[mt][1]);
+        }
+    }
+    // X = beta (V - Gamma Z); then the next chunk's values are requested.
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 a = lds_a_perm(&sm.K[0][0], RP, 16 * mt + m, kk, g);
-            z0 = mfma16(a, Sb[kk][0], z0);
-            z1 = mfma16(a, Sb[kk][1], z1);
-        }
-        const int r0 = 16 * mt + 4 * g;
-        const f32x4 Gr = *reinterpret_cast<const f32x4*>(&sm.Gam[r0]);
-        const f32x4 Br = *reinterpret_cast<const f32x4*>(&sm.bet[r0]);
+        const f32x4 Gr = *reinterpret_cast<const f32x4*>(&F.Gam[16 * mt + 4 * g]);
+        const f32x4 Br = *reinterpret_cast<const f32x4*>(&F.bet[16 * mt + 4 * g]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float v0 = 0.f, v1 = 0.f;
             if (WITH_V) {
-                v0 = bf16_bits_to_float(sm.V[r0 + e][cw + m]);
-                v1 = bf16_bits_to_float(sm.V[r0 + e][cw + 16 + m]);
+                v0 = __uint_as_float(vr[4 * mt + e] << 16);
+                v1 = __uint_as_float(vr[4 * mt + e] & 0xFFFF0000u);
             }
-            BR[mt][0][e] = Br[e] * (v0 - Gr[e] * z0[e]);
-            BR[mt][1][e] = Br[e] * (v1 - Gr[e] * z1[e]);
+            X[mt][0][e] = Br[e] * (v0 - Gr[e] * X[mt][0][e]);
+            X[mt][1][e] = Br[e] * (v1 - Gr[e] * X[mt][1][e]);
         }
     }
-    bf16x8 Bb[2][2];
+    if (WITH_V) chain_fetch_v(vr, vnext, ncn, ldv, g, m);
+    // U by 16-row blocks; the S update's operands exp(gamma_last - gamma) U
+    // are packed as soon as a pair of blocks is done.
+    i16x4 Ub[4][2];
+    bf16x8 Wb[2][2];
+    f32x4 Uprev[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int b = 0; b < 4; ++b) {
+        f32x4 acc0 = X[b][0], acc1 = X[b][1];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) Bb[kk][nt] = pack_acc_pair(BR[2 * kk][nt], BR[2 * kk + 1][nt]);
-    // U = Tm (beta R); Tm is lower triangular, so token tiles 0 and 1 need reduction step 0 only.
-    f32x4 U[4][2];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 a0 = lds_a_perm(&sm.T[0][0], CP, 16 * mt + m, 0, g);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) U[mt][nt] = mfma16(a0, Bb[0][nt], f32x4{0.f, 0.f, 0.f, 0.f});
-        if (mt >= 2) {
-            const bf16x8 a1 = lds_a_perm(&sm.T[0][0], CP, 16 * mt + m, 1, g);
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) U[mt][nt] = mfma16(a1, Bb[1][nt], U[mt][nt]);
+        for (int bp = 0; bp < b; ++bp) {
+            const i16x4 a = lds_blk_a(F.An[b * (b - 1) / 2 + bp], g, m);
+            acc0 = mfma_x16(a, Ub[bp][0], acc0);
+            acc1 = mfma_x16(a, Ub[bp][1], acc1);
+        }
+        const i16x4 a = lds_blk_a(F.Td[b], g, m);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 u0 = mfma_x16(a, pack4(acc0), zero);
+        const f32x4 u1 = mfma_x16(a, pack4(acc1), zero);
+        Ub[b][0] = pack4(u0);
+        Ub[b][1] = pack4(u1);
+        if (b & 1) {
+            const int kk = b >> 1;
+            const f32x4 d0 = *reinterpret_cast<const f32x4*>(&F.Dec[32 * kk + 4 * g]);
+            const f32x4 d1 = *reinterpret_cast<const f32x4*>(&F.Dec[32 * kk + 16 + 4 * g]);
+            Wb[kk][0] = pack_acc_pair(d0 * Uprev[0], d1 * u0);
+            Wb[kk][1] = pack_acc_pair(d0 * Uprev[1], d1 * u1);
+        } else {
+            Uprev[0] = u0;
+            Uprev[1] = u1;
         }
     }
     if (WITH_OUT) {
-        // O = scale (Gamma (Q S^T) + P U), written for the rows of this chunk.
-        bf16x8 Ub[2][2];
+        // O = scale (Gamma (Q S^T) + P U); S is still the chunk's entry state.
+        f32x4 Y[4][2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) Ub[kk][nt] = pack_acc_pair(U[2 * kk][nt], U[2 * kk + 1][nt]);
+            for (int nt = 0; nt < 2; ++nt) Y[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 sb0 = pack_acc_pair(ST[2 * kk][0], ST[2 * kk + 1][0]);
+            const bf16x8 sb1 = pack_acc_pair(ST[2 * kk][1], ST[2 * kk + 1][1]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8 a = lds_a_perm(Q, RP, 16 * mt + m, kk, g);
+                Y[mt][0] = mfma16(a, sb0, Y[mt][0]);
+                Y[mt][1] = mfma16(a, sb1, Y[mt][1]);
+            }
+        }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            f32x4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 Gr = *reinterpret_cast<const f32x4*>(&F.Gam[16 * mt + 4 * g]);
+            f32x4 y0 = Gr * Y[mt][0], y1 = Gr * Y[mt][1];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 a = lds_a_perm(&sm.Q[0][0], RP, 16 * mt + m, kk, g);
-                y0 = mfma16(a, Sb[kk][0], y0);
-                y1 = mfma16(a, Sb[kk][1], y1);
+            for (int b = 0; b <= mt; ++b) {
+                const i16x4 a = lds_blk_a(F.P[mt * (mt + 1) / 2 + b], g, m);
+                y0 = mfma_x16(a, Ub[b][0], y0);
+                y1 = mfma_x16(a, Ub[b][1], y1);
             }
-            const int r0 = 16 * mt + 4 * g;
-            const f32x4 Gr = *reinterpret_cast<const f32x4*>(&sm.Gam[r0]);
-            y0 = Gr * y0;
-            y1 = Gr * y1;
+            const uint32_t off = (uint32_t)(4 * g * ldv + 2 * m) * 2u;
 #pragma unroll
-            for (int kk = 0; kk <= (mt >> 1); ++kk) {
-                const bf16x8 a = lds_a_perm(&sm.P[0][0], CP, 16 * mt + m, kk, g);
-                y0 = mfma16(a, Ub[kk][0], y0);
-                y1 = mfma16(a, Ub[kk][1], y1);
-            }
-            uint16_t* orow = orow0 + (int64_t)r0 * ldv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (nc == kChunk || r0 + e < nc) {
-                    orow[e * ldv] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(scale * y0[e]));
-                    orow[e * ldv + 16] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(scale * y1[e]));
-                }
-            }
+            for (int e = 0; e < 4; ++e)
+                if (nc == kChunk || 16 * mt + 4 * g + e < nc)
+                    st_at<uint32_t>(orow0 + (16 * mt + e) * ldv, off, pack_bf16(scale * y0[e], scale * y1[e]));
         }
     }
     // S^T = Gamma_last S^T + K^T (exp(gamma_last - gamma) U)
-    bf16x8 Wb[2][2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&sm.Dec[32 * kk + 4 * g]);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&sm.Dec[32 * kk + 16 + 4 * g]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) Wb[kk][nt] = pack_acc_pair(d0 * U[2 * kk][nt], d1 * U[2 * kk + 1][nt]);
-    }
-    const float Glast = sm.Gam[kChunk - 1];
+    const float Glast = F.Gam[kChunk - 1];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const bf16x8 a0 = lds_kt_tr(&sm.K[0][0], RP, t, 0, g, m);
-        const bf16x8 a1 = lds_kt_tr(&sm.K[0][0], RP, t, 1, g, m);
+        const bf16x8 a0 = lds_kt_tr(K, RP, t, 0, g, m);
+        const bf16x8 a1 = lds_kt_tr(K, RP, t, 1, g, m);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             f32x4 acc = ST[t][nt] * Glast;
@@ -340,15 +417,51 @@ __device__ __forceinline__ void seg_chain(SegSmem& sm, f32x4 (&ST)[8][2], int cw
     }
 }
 
+// The chain waves' chunk loop (one barrier per chunk, matching the producers).
+// Output pass: one chain with values and outputs. Map pass: the H chain (with
+// values) and, when `with_m`, the M chain (no values) for the same columns.
 template <int MODE>
-__global__ __launch_bounds__(MODE == kModeOut ? 256 : 512) void segment_kernel(
+__device__ __forceinline__ void chain_loop(SegSmem<MODE>& sm, f32x4 (&ST)[8][2], f32x4 (&SM)[8][2], bool with_m,
+                                           const uint16_t* vcol, uint16_t* ocol, int64_t bos, int64_t eos,
+                                           int64_t c_begin, int64_t nchunks, int ldv, float scale, int lg, int lm) {
+    auto chunk_nc = [&](int64_t c) {
+        const int64_t rem = eos - (bos + c * kChunk);
+        return (int)(rem < kChunk ? rem : kChunk);
+    };
+    uint32_t vr[16];
+    if (nchunks > 0) chain_fetch_v(vr, vcol + (bos + c_begin * kChunk) * ldv, chunk_nc(c_begin), ldv, lg, lm);
+    lds_barrier();   // prologue: chunks 0 and 1 staged
+    lds_barrier();   // prologue: chunk 0's factors
+    for (int64_t i = 0; i < nchunks; ++i) {
+        const int64_t c = c_begin + i;
+        const int kb = (int)(i % 3);
+        const int64_t cn = (i + 1 < nchunks) ? c + 1 : c;
+        const int64_t t0 = bos + c * kChunk;
+        const uint16_t* vnext = vcol + (bos + cn * kChunk) * ldv;
+        if (MODE == kModeOut) {
+            chain_step<true, true>(&sm.K[kb][0][0], &sm.Q[kb][0][0], sm.F[i & 1], ST, vr, vnext, chunk_nc(cn),
+                                   ocol + t0 * ldv, ldv, chunk_nc(c), scale, lg, lm);
+        } else {
+            chain_step<true, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], ST, vr, vnext, chunk_nc(cn), nullptr, ldv,
+                                    chunk_nc(c), scale, lg, lm);
+            __builtin_amdgcn_sched_barrier(0);   // keep the H and M steps' temporaries apart
+            if (with_m)
+                chain_step<false, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], SM, vr, nullptr, 0, nullptr, ldv,
+                                         chunk_nc(c), scale, lg, lm);
+        }
+        lds_barrier();
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(64 * (ChainWaves<MODE>::n + kProd)) void segment_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* initial_state,
     const int32_t* __restrict__ cu, float* final_state, uint16_t* __restrict__ out, float* __restrict__ segws,
     int64_t total_tokens, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads, int32_t L, int64_t num_segs,
     float scale) {
-    constexpr int NT = (MODE == kModeOut) ? 256 : 512;
-    __shared__ SegSmem sm;
+    constexpr int NCW = ChainWaves<MODE>::n;
+    __shared__ SegSmem<MODE> sm;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, lg = lane >> 4, lm = lane & 15;
@@ -375,90 +488,107 @@ __global__ __launch_bounds__(MODE == kModeOut ? 256 : 512) void segment_kernel(
     if (MODE == kModeHM && j == nseg - 1) return;            // the last segment needs no map
     const int64_t c_begin = j * L;
     const int64_t c_end = (c_begin + L < nch) ? c_begin + L : nch;
+    const int64_t nchunks = c_end - c_begin;
     float* segmat = segws + ((size_t)sg * num_v_heads + h) * kSegMats * kSegMat;
 
-    // Chain of this wave: OUT: the state from its true entry value; HM: waves
-    // 0-3 the H map (from the initial state in segment 0, else from 0), waves
-    // 4-7 the M map (from I, without values; not needed in segment 0).
-    const bool mchain = (MODE == kModeHM) && w >= 4;
-    const int cw = 32 * (w & 3);
-    f32x4 ST[8][2];
-    const float* src = nullptr;
-    if (MODE == kModeOut)
-        src = (j == 0) ? (initial_state ? initial_state + ((int64_t)n * num_v_heads + h) * kSegMat : nullptr)
-                       : segmat + 2 * kSegMat;
-    if (MODE == kModeHM && !mchain && j == 0 && initial_state)
-        src = initial_state + ((int64_t)n * num_v_heads + h) * kSegMat;
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int col = cw + 16 * nt + lm;
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if (mchain) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s[e] = (16 * t + 4 * lg + e == col) ? 1.f : 0.f;
-            } else if (src) {
-                s = *reinterpret_cast<const f32x4*>(src + (int64_t)col * D + 16 * t + 4 * lg);
-            }
-            ST[t][nt] = s;
-        }
-
-    // Upper block triangles of Tm and P stay zero for every chunk.
-    for (int e = tid; e < kChunk * kChunk; e += NT) {
-        const int r = e >> 6, c = e & 63;
-        if ((c >> 4) > (r >> 4)) {
-            sm.T[r][c] = 0;
-            sm.P[r][c] = 0;
-        }
-    }
+    const bool producer = w >= NCW;
+    const int pw = w - NCW;
+    const int pl = tid - 64 * NCW;
+    // Chain waves (0-3): pass C: the state from its true entry value; pass A:
+    // the H map (from the initial state in segment 0, else from 0) and, from
+    // segment 1 on, the M map (from I, without values).
+    const int cb = 32 * (w & 3);
 
     const int ldk = num_qk_heads * D, ldv = num_v_heads * D;
-    SegPrefetch<NT> pf;
-    auto fetch = [&](int64_t c) {
-        const int64_t t0 = sr.bos + c * kChunk;
-        const int nc = (int)((sr.eos - t0) < kChunk ? (sr.eos - t0) : kChunk);
-        seg_fetch<MODE, NT>(pf, k + t0 * ldk + hq * D, q + t0 * ldk + hq * D, v + t0 * ldv + h * D,
-                            g + t0 * num_v_heads + h, beta + t0 * num_v_heads + h, nc, ldk, ldv, num_v_heads, tid);
-        return nc;
+    auto chunk_t0 = [&](int64_t c) { return sr.bos + c * kChunk; };
+    auto chunk_nc = [&](int64_t c) {
+        const int64_t rem = sr.eos - chunk_t0(c);
+        return (int)(rem < kChunk ? rem : kChunk);
     };
-    if (c_begin < c_end) {
-        const int nc0 = fetch(c_begin);
-        seg_stage<MODE, NT>(sm, pf, nc0, tid, w);
-    }
-    __syncthreads();
-
-    for (int64_t c = c_begin; c < c_end; ++c) {
-        const int64_t t0 = sr.bos + c * kChunk;
-        const int nc = (int)((sr.eos - t0) < kChunk ? (sr.eos - t0) : kChunk);
-        // Next chunk's operands (the last chunk re-reads itself: no branch around loads).
-        const int ncn = fetch((c + 1 < c_end) ? c + 1 : c);
-
-        seg_prep<MODE, NT>(sm, tid, w, lg, lm);
-        if (MODE == kModeOut) {
-            seg_chain<true, true>(sm, ST, cw, lg, lm, out + t0 * ldv + h * D + cw + lm, ldv, nc, scale);
-        } else if (mchain) {
-            if (j > 0) seg_chain<false, false>(sm, ST, cw, lg, lm, nullptr, ldv, nc, scale);
-        } else {
-            seg_chain<true, false>(sm, ST, cw, lg, lm, nullptr, ldv, nc, scale);
+    auto clampc = [&](int64_t c) { return c < c_end ? c : c_end - 1; };
+    ProdRegs pr;
+    auto fetch_kq = [&](int64_t c) {
+        const int64_t t0 = chunk_t0(c);
+        prod_fetch_kq<MODE>(pr, k + t0 * ldk + hq * D, q + t0 * ldk + hq * D, chunk_nc(c), ldk, pl);
+    };
+    auto fetch_gb = [&](int64_t c) {
+        const int64_t t0 = chunk_t0(c);
+        prod_fetch_gb(pr, g + t0 * num_v_heads + h, beta + t0 * num_v_heads + h, chunk_nc(c), num_v_heads, lane);
+    };
+    if (producer) {
+        // Prologue: chunks 0 and 1 of the segment staged, chunk 0's factors built.
+        if (nchunks > 0) {
+            fetch_kq(c_begin);
+            fetch_gb(c_begin);
+            prod_stage_kq<MODE>(sm, 0, pr, chunk_nc(c_begin), pl);
+            fetch_kq(clampc(c_begin + 1));
+            if (nchunks > 1) prod_stage_kq<MODE>(sm, 1, pr, chunk_nc(c_begin + 1), pl);
         }
-        __syncthreads();                       // every wave is done with this chunk's operands
-        seg_stage<MODE, NT>(sm, pf, ncn, tid, w);
-        __syncthreads();
+        lds_barrier();
+        if (nchunks > 0) {
+            prod_factors<MODE>(sm, 0, sm.F[0], pr, chunk_nc(c_begin), pw, lane);
+            fetch_kq(clampc(c_begin + 2));
+            fetch_gb(clampc(c_begin + 1));
+        }
+        lds_barrier();
+        for (int64_t i = 0; i < nchunks; ++i) {
+            const int64_t c = c_begin + i;
+            // chunk c + 1: factors (its tiles were staged two steps ago);
+            // chunk c + 2: tiles from registers to LDS; then the next loads.
+            if (i + 1 < nchunks)
+                prod_factors<MODE>(sm, (int)((i + 1) % 3), sm.F[(i + 1) & 1], pr, chunk_nc(c + 1), pw, lane);
+            if (i + 2 < nchunks) prod_stage_kq<MODE>(sm, (int)((i + 2) % 3), pr, chunk_nc(c + 2), pl);
+            fetch_kq(clampc(c + 3));
+            fetch_gb(clampc(c + 2));
+            lds_barrier();
+        }
+        return;
     }
-
-    float* dst = nullptr;
-    if (MODE == kModeOut)
-        dst = (j == nseg - 1 && final_state) ? final_state + ((int64_t)n * num_v_heads + h) * kSegMat : nullptr;
-    if (MODE == kModeHM) dst = mchain ? (j > 0 ? segmat + kSegMat : nullptr) : segmat;
-    if (dst) {
+    // Chain waves.
+    f32x4 ST[8][2], SM[8][2];
+    {
+        const float* src = nullptr;
+        if (MODE == kModeOut)
+            src = (j == 0) ? (initial_state ? initial_state + ((int64_t)n * num_v_heads + h) * kSegMat : nullptr)
+                           : segmat + 2 * kSegMat;
+        if (MODE == kModeHM && j == 0 && initial_state) src = initial_state + ((int64_t)n * num_v_heads + h) * kSegMat;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-                *reinterpret_cast<f32x4*>(dst + (int64_t)(cw + 16 * nt + lm) * D + 16 * t + 4 * lg) = ST[t][nt];
+            for (int nt = 0; nt < 2; ++nt) {
+                const int col = cb + 2 * lm + nt;
+                f32x4 s = {0.f, 0.f, 0.f, 0.f}, e1;
+                if (src) s = *reinterpret_cast<const f32x4*>(src + (int64_t)col * D + 16 * t + 4 * lg);
+                ST[t][nt] = s;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) e1[e] = (16 * t + 4 * lg + e == col) ? 1.f : 0.f;
+                SM[t][nt] = e1;
+            }
+    }
+    chain_loop<MODE>(sm, ST, SM, MODE == kModeHM && j > 0, v + h * D + cb, out + h * D + cb, sr.bos, sr.eos,
+                     c_begin, nchunks, ldv, scale, lg, lm);
+
+    if (MODE == kModeOut) {
+        if (j == nseg - 1 && final_state) {
+            float* dst = final_state + ((int64_t)n * num_v_heads + h) * kSegMat;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    *reinterpret_cast<f32x4*>(dst + (int64_t)(cb + 2 * lm + nt) * D + 16 * t + 4 * lg) = ST[t][nt];
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int64_t o = (int64_t)(cb + 2 * lm + nt) * D + 16 * t + 4 * lg;
+                *reinterpret_cast<f32x4*>(segmat + o) = ST[t][nt];
+                if (j > 0) *reinterpret_cast<f32x4*>(segmat + kSegMat + o) = SM[t][nt];
+            }
     }
 }
+
 
 // Combine, fp32: for each (sequence, V head, block of 16 state rows), walk the
 // sequence's segments: S_in(1) = H_0, S_in(j+1) = S_in(j) M_j + H_j; S_in(j) is
@@ -545,7 +675,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     // Pass A and the combine are needed only when some sequence spans more than one segment.
     if (a.num_seqs > 1 || a.total_tokens > (int64_t)kChunk * L) {
         prof::begin(stream, "gdn_segment_maps");
-        hipLaunchKernelGGL((segment_kernel<kModeHM>), grid, dim3(512), 0, stream, q, k, v, a.g, a.beta,
+        hipLaunchKernelGGL((segment_kernel<kModeHM>), grid, dim3(64 * (ChainWaves<kModeHM>::n + kProd)), 0, stream, q, k, v, a.g, a.beta,
                            a.initial_state, a.cu_seqlens, a.final_state, (uint16_t*)a.out, seg_ws, a.total_tokens,
                            a.num_seqs, a.num_qk_heads, a.num_v_heads, L, segs, a.scale);
         prof::end(stream);
@@ -557,7 +687,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     prof::begin(stream, "gdn_segment_out");
-    hipLaunchKernelGGL((segment_kernel<kModeOut>), grid, dim3(256), 0, stream, q, k, v, a.g, a.beta,
+    hipLaunchKernelGGL((segment_kernel<kModeOut>), grid, dim3(64 * (ChainWaves<kModeOut>::n + kProd)), 0, stream, q, k, v, a.g, a.beta,
                        a.initial_state, a.cu_seqlens, a.final_state, (uint16_t*)a.out, seg_ws, a.total_tokens,
                        a.num_seqs, a.num_qk_heads, a.num_v_heads, L, segs, a.scale);
     prof::end(stream);
