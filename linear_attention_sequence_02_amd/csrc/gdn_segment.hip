@@ -45,7 +45,8 @@ constexpr size_t kSegMat = (size_t)D * D;   // floats in one 128 x 128 matrix
 constexpr int kSegMats = 3;                 // H, M, S_in per (segment, V head)
 constexpr int kProd = 4;                    // producer waves per workgroup
 constexpr int TP = 20;                      // bf16 row pitch of the 16 x 16 factor blocks
-constexpr int AP = 20;                      // fp32 row pitch of a producer's diagonal A block
+constexpr int AP = 20;                      // fp32 row pitch of a diagonal A block
+constexpr int AB = 16 * AP + 8;             // fp32 stride between diagonal A blocks (bank offset 8)
 
 template <int MODE>
 struct ChainWaves {
@@ -74,9 +75,10 @@ __device__ __forceinline__ int find_seq_for_seg(const int32_t* cu, int N, int64_
 // token 16 b + r), read by the chain as 16x16x16 MFMA A operands.
 struct __attribute__((aligned(16))) ChunkFactors {
     uint16_t Td[4][16][TP];     // (I + A_bb)^-1
+    uint16_t Tw[4][16][TP];     // diag(exp(gamma_last - gamma)) (I + A_bb)^-1: the state update's rows
     uint16_t An[6][16][TP];     // -A_bb' for b > b', at b (b - 1) / 2 + b'
-    uint16_t P[10][16][TP];     // P blocks (mt >= nt), at mt (mt + 1) / 2 + nt (output pass)
-    float Gam[kChunk], Dec[kChunk], bet[kChunk];
+    uint16_t P[10][16][TP];     // scale * P blocks (mt >= nt), at mt (mt + 1) / 2 + nt (output pass)
+    float Gam[kChunk], Gs[kChunk], bet[kChunk];   // Gamma, scale * Gamma, beta
 };
 
 template <int MODE>
@@ -84,19 +86,39 @@ struct __attribute__((aligned(16))) SegSmem {
     uint16_t K[3][kChunk][RP];                          // keys, token-major
     uint16_t Q[(MODE == kModeOut) ? 3 : 1][kChunk][RP]; // queries (output pass)
     ChunkFactors F[2];
-    float Ad[kProd][16][AP];                            // producer scratch: diagonal block of A
+    float Ad[4 * AB];                                   // producer scratch: the diagonal blocks of A
+    float Dec[kChunk];                                  // producer scratch: exp(gamma_last - gamma)
     float pg[kProd][kChunk], pb[kProd][kChunk];         // producer scratch: gamma, beta
 };
 
-// Global access as wave-uniform base + 32-bit byte offset (the SGPR-base form
-// of global loads and stores: one address VGPR instead of two).
+// A pointer the compiler must keep in SGPRs (so that per-row bases are not
+// folded into per-lane 64-bit addresses).
 template <class T>
-__device__ __forceinline__ T ld_at(const void* base, uint32_t byte_off) {
-    return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
 }
-template <class T>
-__device__ __forceinline__ void st_at(void* base, uint32_t byte_off, T x) {
-    *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off) = x;
+
+// Raw buffer access to one chunk's rows (word 3 of the resource: 32-bit data
+// format, as the GFX9 buffer resource layout requires for untyped access).
+// Reads at or past `bytes` return 0 and stores there are dropped, so a partial
+// last chunk needs neither clamped rows nor guarded stores, and no access can
+// leave the chunk's valid rows.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t chunk_rsrc(const void* base, int64_t bytes) {
+    const uint32_t n = bytes > 0 ? (uint32_t)bytes : 0u;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ uint32_t buf_ld_b32(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x4 buf_ld_b128(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_st_b32(uint32_t x, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(x, r, (int)off, 0, 0);
 }
 
 // Producer registers: K (and Q) 16-byte pieces of the chunk two ahead, and g,
@@ -108,47 +130,51 @@ struct ProdRegs {
 
 // Rows past the end of a chunk re-read its last row (they are zeroed when
 // staged), so no load leaves the sequence and none is branched.
-// Piece i of producer lane pl: row 16 i + pl / 16, 16-byte column block pl % 16.
+// Piece i of producer lane pl: row 16 i + pl / 16, 16-byte column block pl %
+// 16. Rows past nc read as zero.
 template <int MODE>
 __device__ __forceinline__ void prod_fetch_kq(ProdRegs& pr, const uint16_t* kc, const uint16_t* qc, int nc, int ldk,
                                               int pl) {
-    const int r0 = pl >> 4;
-    if (nc == kChunk) {
-        const uint32_t off = (uint32_t)(r0 * ldk + (pl & 15) * 8) * 2u;
+    const rsrc_t rk = chunk_rsrc(uniform_ptr(kc), (int64_t)nc * ldk * 2);
+    const rsrc_t rq = chunk_rsrc(uniform_ptr(qc), (int64_t)nc * ldk * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pr.k[i] = ld_at<u32x4>(kc + 16 * i * ldk, off);
-            if (MODE == kModeOut) pr.q[i] = ld_at<u32x4>(qc + 16 * i * ldk, off);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = r0 + 16 * i;
-            const uint32_t off = (uint32_t)((row < nc ? row : nc - 1) * ldk + (pl & 15) * 8) * 2u;
-            pr.k[i] = ld_at<u32x4>(kc, off);
-            if (MODE == kModeOut) pr.q[i] = ld_at<u32x4>(qc, off);
-        }
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (uint32_t)(((pl >> 4) + 16 * i) * ldk + (pl & 15) * 8) * 2u;
+        pr.k[i] = buf_ld_b128(rk, off);
+        if (MODE == kModeOut) pr.q[i] = buf_ld_b128(rq, off);
     }
 }
 
 __device__ __forceinline__ void prod_fetch_gb(ProdRegs& pr, const float* gc, const float* bc, int nc, int hv,
                                               int lane) {
-    const uint32_t off = (uint32_t)((lane < nc ? lane : nc - 1) * hv) * 4u;
-    pr.g = ld_at<float>(gc, off);
-    pr.b = ld_at<float>(bc, off);
+    const uint32_t off = (uint32_t)(lane * hv) * 4u;
+    pr.g = __builtin_bit_cast(float, buf_ld_b32(chunk_rsrc(uniform_ptr(gc), (int64_t)nc * hv * 4), off));
+    pr.b = __builtin_bit_cast(float, buf_ld_b32(chunk_rsrc(uniform_ptr(bc), (int64_t)nc * hv * 4), off));
 }
 
+// Rows past the end of a partial chunk were read as zero.
 template <int MODE>
-__device__ __forceinline__ void prod_stage_kq(SegSmem<MODE>& sm, int buf, const ProdRegs& pr, int nc, int pl) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
+__device__ __forceinline__ void prod_stage_kq(SegSmem<MODE>& sm, int buf, const ProdRegs& pr, int pl) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int p = pl + 256 * i;
         const int row = p >> 4, c8 = p & 15;
-        const bool in = row < nc;
-        *reinterpret_cast<u32x4*>(&sm.K[buf][row][c8 * 8]) = in ? pr.k[i] : z;
-        if (MODE == kModeOut) *reinterpret_cast<u32x4*>(&sm.Q[buf][row][c8 * 8]) = in ? pr.q[i] : z;
+        *reinterpret_cast<u32x4*>(&sm.K[buf][row][c8 * 8]) = pr.k[i];
+        if (MODE == kModeOut) *reinterpret_cast<u32x4*>(&sm.Q[buf][row][c8 * 8]) = pr.q[i];
     }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts inside
+// rows of 16 lanes, then the row totals carried by the GFX9 row broadcasts.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    // row_shr:d (DPP control 0x110 + d); lanes below d in their row add 0.
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xC, 0xF, false));
+    return x;
 }
 
 // 16 x 16 Gram block: rows 16 mt .. of X times rows 16 nt .. of K, transposed;
@@ -166,52 +192,98 @@ __device__ __forceinline__ void store_block_bf16(uint16_t (*blk)[TP], const f32x
     for (int e = 0; e < 4; ++e) blk[4 * g + e][m] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[e]));
 }
 
-// Factors of one chunk (its K/Q tiles in buffer kb) into F: producer wave pw
-// owns diagonal block pw (Gram, mask, inverse) and jobs pw, pw + 4, ... of the
-// off-diagonal A blocks (jobs 0..5) and the P blocks (jobs 6..15).
+// Factors of one chunk (its K/Q tiles in buffer kb) into F. Producer wave 0
+// builds the four diagonal blocks of A and inverts them (lane group g: block
+// g, lane m: column m); waves 1..3 take the off-diagonal A blocks (jobs 0..5)
+// and the P blocks (jobs 6..15) in turn.
 template <int MODE>
 __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFactors& F, const ProdRegs& pr, int nc,
-                                             int pw, int lane) {
+                                             float scale, int pw, int lane) {
     const uint16_t* K = &sm.K[kb][0][0];
     const uint16_t* Q = &sm.Q[(MODE == kModeOut) ? kb : 0][0][0];
     const int g = lane >> 4, m = lane & 15;
 
     // gamma = in-chunk inclusive prefix sum of g; rows past nc add 0 and have beta 0.
-    float x = lane < nc ? pr.g : 0.f;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
-    }
+    const float x = wave_prefix_sum(lane < nc ? pr.g : 0.f);
     const float bt = lane < nc ? pr.b : 0.f;
     sm.pg[pw][lane] = x;
     sm.pb[pw][lane] = bt;
+
     if (pw == 0) {
         const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
-        F.Gam[lane] = fast_exp(x);
-        F.Dec[lane] = fast_exp(glast - x);
+        const float G = fast_exp(x);
+        F.Gam[lane] = G;
+        F.Gs[lane] = scale * G;
         F.bet[lane] = bt;
-    }
-
-    // Diagonal block pw of A, fp32, strictly lower.
-    {
-        const f32x4 acc = gram_block(K, K, pw, pw, g, m);
-        const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[pw][16 * pw + 4 * g]);
-        const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[pw][16 * pw + 4 * g]);
-        const float gc = sm.pg[pw][16 * pw + m];
+        sm.Dec[lane] = fast_exp(glast - x);
+        // Diagonal blocks of A, fp32, strictly lower: block b = rows/cols 16 b ..
+        float* Ad = sm.Ad;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float a = br[e] * fast_exp(gr[e] - gc) * acc[e];
-            sm.Ad[pw][4 * g + e][m] = (m < 4 * g + e) ? a : 0.f;
+        for (int b = 0; b < 4; ++b) {
+            const f32x4 acc = gram_block(K, K, b, b, g, m);
+            const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[0][16 * b + 4 * g]);
+            const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[0][16 * b + 4 * g]);
+            const float gc = sm.pg[0][16 * b + m];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = br[e] * fast_exp(gr[e] - gc) * acc[e];
+                Ad[b * AB + (4 * g + e) * AP + m] = (m < 4 * g + e) ? a : 0.f;
+            }
         }
+        // (I + A_gg)^-1, column m, by forward substitution in batches of four
+        // rows: a batch reads its rows as 16-byte pieces, takes the part of
+        // each row's sum over earlier batches in parallel, then the four rows
+        // in order.
+        const float* Ag = Ad + g * AB;
+        float t[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f32x4 a[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c4 = 0; c4 <= q; ++c4) a[i][c4] = *reinterpret_cast<const f32x4*>(Ag + (4 * q + i) * AP + 4 * c4);
+            float sacc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * q + i;
+                float p0 = (r == m) ? 1.f : 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+                for (int c4 = 0; c4 < q; ++c4) {
+                    p0 -= a[i][c4][0] * t[4 * c4];
+                    p1 -= a[i][c4][1] * t[4 * c4 + 1];
+                    p2 -= a[i][c4][2] * t[4 * c4 + 2];
+                    p3 -= a[i][c4][3] * t[4 * c4 + 3];
+                }
+                sacc[i] = (p0 + p1) + (p2 + p3);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = sacc[i];
+#pragma unroll
+                for (int jj = 0; jj < i; ++jj) v -= a[i][q][jj] * t[4 * q + jj];
+                t[4 * q + i] = v;
+            }
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 dec = *reinterpret_cast<const f32x4*>(&sm.Dec[16 * g + 4 * r4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * r4 + e;
+                F.Td[g][r][m] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(t[r]));
+                F.Tw[g][r][m] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dec[e] * t[r]));
+            }
+        }
+        return;
     }
 
-    // Off-diagonal A blocks (stored negated) and P blocks.
+    // Off-diagonal A blocks (stored negated) and P blocks (scaled).
     constexpr uint64_t kRow = 0x3333222110333221ull, kCol = 0x3210210100210100ull;
     constexpr int NJOBS = (MODE == kModeOut) ? 16 : 6;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        const int job = pw + 4 * jj;
+    for (int jj = 0; jj < 6; ++jj) {
+        const int job = (pw - 1) + 3 * jj;
         if (job < NJOBS) {
             const int mt = (int)((kRow >> (4 * job)) & 15), nt = (int)((kCol >> (4 * job)) & 15);
             const bool isP = job >= 6;
@@ -222,7 +294,7 @@ __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFac
             if (isP) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float p = fast_exp(gr[e] - gc) * acc[e];
+                    const float p = scale * fast_exp(gr[e] - gc) * acc[e];
                     v[e] = (mt > nt || m <= 4 * g + e) ? p : 0.f;
                 }
                 store_block_bf16(F.P[job - 6], v, g, m);
@@ -234,27 +306,6 @@ __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFac
             }
         }
     }
-
-    // (I + A_pw)^-1 by forward substitution: lane (g, m) computes column m
-    // (the four lane groups redundantly) and stores rows 4 g .. 4 g + 3.
-    float t[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        float p0 = (r == m) ? 1.f : 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-        for (int j = 0; j < r; ++j) {
-            const float term = sm.Ad[pw][r][j] * t[j];
-            if ((j & 3) == 0) p0 -= term;
-            else if ((j & 3) == 1) p1 -= term;
-            else if ((j & 3) == 2) p2 -= term;
-            else p3 -= term;
-        }
-        t[r] = (p0 + p1) + (p2 + p3);
-    }
-    f32x4 col;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) col[e] = g == 0 ? t[e] : g == 1 ? t[4 + e] : g == 2 ? t[8 + e] : t[12 + e];
-    store_block_bf16(F.Td[pw], col, g, m);
 }
 
 __device__ __forceinline__ i16x4 lds_blk_a(const uint16_t (*blk)[TP], int g, int m) {
@@ -274,23 +325,14 @@ __device__ __forceinline__ i16x4 pack4(const f32x4& v) {
 }
 
 // Chain-wave values: rows 16 mt + 4 g + e, columns cb + 2 m, cb + 2 m + 1 of
-// the chunk whose (row 0, column cb) element vc points at (wave-uniform).
+// the chunk whose (row 0, column cb) element vc points at (wave-uniform);
+// rows past nc read as zero.
 __device__ __forceinline__ void chain_fetch_v(uint32_t (&vr)[16], const uint16_t* vc, int nc, int ldv, int g, int m) {
-    if (nc == kChunk) {
-        const uint32_t off = (uint32_t)(4 * g * ldv + 2 * m) * 2u;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
+        const rsrc_t r = chunk_rsrc(uniform_ptr(vc + (int64_t)16 * mt * ldv), (int64_t)(nc - 16 * mt) * ldv * 2);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) vr[4 * mt + e] = ld_at<uint32_t>(vc + (16 * mt + e) * ldv, off);
-    } else {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * mt + 4 * g + e;
-                const uint32_t off = (uint32_t)((row < nc ? row : nc - 1) * ldv + 2 * m) * 2u;
-                vr[4 * mt + e] = ld_at<uint32_t>(vc, off);
-            }
+        for (int e = 0; e < 4; ++e) vr[4 * mt + e] = buf_ld_b32(r, (uint32_t)((4 * g + e) * ldv + 2 * m) * 2u);
     }
 }
 
@@ -335,12 +377,17 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
             X[mt][1][e] = Br[e] * (v1 - Gr[e] * X[mt][1][e]);
         }
     }
+    // The next chunk's values are requested only after this chunk's are
+    // consumed: global loads complete in order, so a load hoisted above the
+    // uses of the previous ones would make those uses wait for it.
+    __builtin_amdgcn_sched_barrier(0);
     if (WITH_V) chain_fetch_v(vr, vnext, ncn, ldv, g, m);
-    // U by 16-row blocks; the S update's operands exp(gamma_last - gamma) U
-    // are packed as soon as a pair of blocks is done.
+    // U by 16-row blocks: U_b = Td_b (X_b - sum A_bb' U_b'), and the state
+    // update's exp(gamma_last - gamma) U_b = Tw_b (same right-hand side),
+    // packed as soon as a pair of blocks is done.
     i16x4 Ub[4][2];
     bf16x8 Wb[2][2];
-    f32x4 Uprev[2];
+    f32x4 Wprev[2];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         f32x4 acc0 = X[b][0], acc1 = X[b][1];
@@ -350,25 +397,24 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
             acc0 = mfma_x16(a, Ub[bp][0], acc0);
             acc1 = mfma_x16(a, Ub[bp][1], acc1);
         }
+        const i16x4 r0 = pack4(acc0), r1 = pack4(acc1);
         const i16x4 a = lds_blk_a(F.Td[b], g, m);
+        const i16x4 aw = lds_blk_a(F.Tw[b], g, m);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 u0 = mfma_x16(a, pack4(acc0), zero);
-        const f32x4 u1 = mfma_x16(a, pack4(acc1), zero);
-        Ub[b][0] = pack4(u0);
-        Ub[b][1] = pack4(u1);
+        Ub[b][0] = pack4(mfma_x16(a, r0, zero));
+        Ub[b][1] = pack4(mfma_x16(a, r1, zero));
+        const f32x4 w0 = mfma_x16(aw, r0, zero);
+        const f32x4 w1 = mfma_x16(aw, r1, zero);
         if (b & 1) {
-            const int kk = b >> 1;
-            const f32x4 d0 = *reinterpret_cast<const f32x4*>(&F.Dec[32 * kk + 4 * g]);
-            const f32x4 d1 = *reinterpret_cast<const f32x4*>(&F.Dec[32 * kk + 16 + 4 * g]);
-            Wb[kk][0] = pack_acc_pair(d0 * Uprev[0], d1 * u0);
-            Wb[kk][1] = pack_acc_pair(d0 * Uprev[1], d1 * u1);
+            Wb[b >> 1][0] = pack_acc_pair(Wprev[0], w0);
+            Wb[b >> 1][1] = pack_acc_pair(Wprev[1], w1);
         } else {
-            Uprev[0] = u0;
-            Uprev[1] = u1;
+            Wprev[0] = w0;
+            Wprev[1] = w1;
         }
     }
     if (WITH_OUT) {
-        // O = scale (Gamma (Q S^T) + P U); S is still the chunk's entry state.
+        // O = scale Gamma (Q S^T) + (scale P) U; S is still the chunk's entry state.
         f32x4 Y[4][2];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -385,9 +431,10 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
                 Y[mt][1] = mfma16(a, sb1, Y[mt][1]);
             }
         }
+        uint32_t ob[4][4];   // bf16 pairs: row 16 mt + 4 g + e, columns cb + 2 m, cb + 2 m + 1
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const f32x4 Gr = *reinterpret_cast<const f32x4*>(&F.Gam[16 * mt + 4 * g]);
+            const f32x4 Gr = *reinterpret_cast<const f32x4*>(&F.Gs[16 * mt + 4 * g]);
             f32x4 y0 = Gr * Y[mt][0], y1 = Gr * Y[mt][1];
 #pragma unroll
             for (int b = 0; b <= mt; ++b) {
@@ -395,11 +442,15 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
                 y0 = mfma_x16(a, Ub[b][0], y0);
                 y1 = mfma_x16(a, Ub[b][1], y1);
             }
-            const uint32_t off = (uint32_t)(4 * g * ldv + 2 * m) * 2u;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (nc == kChunk || 16 * mt + 4 * g + e < nc)
-                    st_at<uint32_t>(orow0 + (16 * mt + e) * ldv, off, pack_bf16(scale * y0[e], scale * y1[e]));
+            for (int e = 0; e < 4; ++e) ob[mt][e] = pack_bf16(y0[e], y1[e]);
+        }
+        // Rows past nc fall outside the chunk's buffer range and are dropped.
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const rsrc_t r = chunk_rsrc(uniform_ptr(orow0 + (int64_t)16 * mt * ldv), (int64_t)(nc - 16 * mt) * ldv * 2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) buf_st_b32(ob[mt][e], r, (uint32_t)((4 * g + e) * ldv + 2 * m) * 2u);
         }
     }
     // S^T = Gamma_last S^T + K^T (exp(gamma_last - gamma) U)
@@ -430,6 +481,10 @@ __device__ __forceinline__ void chain_loop(SegSmem<MODE>& sm, f32x4 (&ST)[8][2],
     };
     uint32_t vr[16];
     if (nchunks > 0) chain_fetch_v(vr, vcol + (bos + c_begin * kChunk) * ldv, chunk_nc(c_begin), ldv, lg, lm);
+    // The entry state and the first values have arrived before the chunk loop
+    // starts; otherwise the loop header's wait for the values would also cover
+    // every later global access (the previous chunk's output stores included).
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     lds_barrier();   // prologue: chunks 0 and 1 staged
     lds_barrier();   // prologue: chunk 0's factors
     for (int64_t i = 0; i < nchunks; ++i) {
@@ -520,13 +575,13 @@ __global__ __launch_bounds__(64 * (ChainWaves<MODE>::n + kProd)) void segment_ke
         if (nchunks > 0) {
             fetch_kq(c_begin);
             fetch_gb(c_begin);
-            prod_stage_kq<MODE>(sm, 0, pr, chunk_nc(c_begin), pl);
+            prod_stage_kq<MODE>(sm, 0, pr, pl);
             fetch_kq(clampc(c_begin + 1));
-            if (nchunks > 1) prod_stage_kq<MODE>(sm, 1, pr, chunk_nc(c_begin + 1), pl);
+            if (nchunks > 1) prod_stage_kq<MODE>(sm, 1, pr, pl);
         }
         lds_barrier();
         if (nchunks > 0) {
-            prod_factors<MODE>(sm, 0, sm.F[0], pr, chunk_nc(c_begin), pw, lane);
+            prod_factors<MODE>(sm, 0, sm.F[0], pr, chunk_nc(c_begin), scale, pw, lane);
             fetch_kq(clampc(c_begin + 2));
             fetch_gb(clampc(c_begin + 1));
         }
@@ -536,8 +591,9 @@ __global__ __launch_bounds__(64 * (ChainWaves<MODE>::n + kProd)) void segment_ke
             // chunk c + 1: factors (its tiles were staged two steps ago);
             // chunk c + 2: tiles from registers to LDS; then the next loads.
             if (i + 1 < nchunks)
-                prod_factors<MODE>(sm, (int)((i + 1) % 3), sm.F[(i + 1) & 1], pr, chunk_nc(c + 1), pw, lane);
-            if (i + 2 < nchunks) prod_stage_kq<MODE>(sm, (int)((i + 2) % 3), pr, chunk_nc(c + 2), pl);
+                prod_factors<MODE>(sm, (int)((i + 1) % 3), sm.F[(i + 1) & 1], pr, chunk_nc(c + 1), scale, pw,
+                                   lane);
+            if (i + 2 < nchunks) prod_stage_kq<MODE>(sm, (int)((i + 2) % 3), pr, pl);
             fetch_kq(clampc(c + 3));
             fetch_gb(clampc(c + 2));
             lds_barrier();
