@@ -44,7 +44,7 @@ enum { kModeOut = 0, kModeHM = 1 };
 constexpr size_t kSegMat = (size_t)D * D;   // floats in one 128 x 128 matrix
 constexpr int kSegMats = 3;                 // H, M, S_in per (segment, V head)
 constexpr int kProd = 4;                    // producer waves per workgroup
-constexpr int TP = 20;                      // bf16 row pitch of the 16 x 16 factor blocks
+constexpr int TP = 24;                      // bf16 pitch of the 16 x 16 factor blocks (48 bytes)
 constexpr int AP = 20;                      // fp32 row pitch of a diagonal A block
 constexpr int AB = 16 * AP + 8;             // fp32 stride between diagonal A blocks (bank offset 8)
 
@@ -71,13 +71,15 @@ __device__ __forceinline__ int find_seq_for_seg(const int32_t* cu, int N, int64_
     return lo;
 }
 
-// One chunk's factors. Blocks are row-major 16 x 16 bf16 (row = the chunk's
-// token 16 b + r), read by the chain as 16x16x16 MFMA A operands.
+// One chunk's factors. A 16 x 16 block X is stored column-major, blk[c][r] =
+// X[r][c] (r: the chunk's token 16 b + r), so that producers write four rows
+// of a column with one 8-byte store and the chain reads its 16x16x16 MFMA A
+// operand with the LDS transpose read.
 struct __attribute__((aligned(16))) ChunkFactors {
     uint16_t Td[4][16][TP];     // (I + A_bb)^-1
     uint16_t Tw[4][16][TP];     // diag(exp(gamma_last - gamma)) (I + A_bb)^-1: the state update's rows
-    uint16_t An[6][16][TP];     // -A_bb' for b > b', at b (b - 1) / 2 + b'
-    uint16_t P[10][16][TP];     // scale * P blocks (mt >= nt), at mt (mt + 1) / 2 + nt (output pass)
+    uint16_t Ob[17][16][TP];    // 0..5: -A_bb' (b > b') at b (b - 1) / 2 + b'; 6..15: scale * P
+                                // blocks (mt >= nt, output pass) at 6 + mt (mt + 1) / 2 + nt; 16: unused
     float Gam[kChunk], Gs[kChunk], bet[kChunk];   // Gamma, scale * Gamma, beta
 };
 
@@ -187,9 +189,13 @@ __device__ __forceinline__ f32x4 gram_block(const uint16_t* X, const uint16_t* K
     return acc;
 }
 
+// Accumulator tile (lane (g, m): rows 4 g .. 4 g + 3 of column m) into a
+// column-major block.
 __device__ __forceinline__ void store_block_bf16(uint16_t (*blk)[TP], const f32x4& v, int g, int m) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) blk[4 * g + e][m] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[e]));
+    u32x2 u;
+    u.x = pack_bf16(v[0], v[1]);
+    u.y = pack_bf16(v[2], v[3]);
+    *reinterpret_cast<u32x2*>(&blk[m][4 * g]) = u;
 }
 
 // Factors of one chunk (its K/Q tiles in buffer kb) into F. Producer wave 0
@@ -265,51 +271,53 @@ __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFac
                 t[4 * q + i] = v;
             }
         }
+        // Column m of both blocks: 16 contiguous bf16 each (two 16-byte stores).
+        u32x4 td[2], tw[2];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const f32x4 dec = *reinterpret_cast<const f32x4*>(&sm.Dec[16 * g + 4 * r4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * r4 + e;
-                F.Td[g][r][m] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(t[r]));
-                F.Tw[g][r][m] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dec[e] * t[r]));
-            }
+            td[r4 >> 1][2 * (r4 & 1)] = pack_bf16(t[4 * r4], t[4 * r4 + 1]);
+            td[r4 >> 1][2 * (r4 & 1) + 1] = pack_bf16(t[4 * r4 + 2], t[4 * r4 + 3]);
+            tw[r4 >> 1][2 * (r4 & 1)] = pack_bf16(dec[0] * t[4 * r4], dec[1] * t[4 * r4 + 1]);
+            tw[r4 >> 1][2 * (r4 & 1) + 1] = pack_bf16(dec[2] * t[4 * r4 + 2], dec[3] * t[4 * r4 + 3]);
         }
+        *reinterpret_cast<u32x4*>(&F.Td[g][m][0]) = td[0];
+        *reinterpret_cast<u32x4*>(&F.Td[g][m][8]) = td[1];
+        *reinterpret_cast<u32x4*>(&F.Tw[g][m][0]) = tw[0];
+        *reinterpret_cast<u32x4*>(&F.Tw[g][m][8]) = tw[1];
         return;
     }
 
-    // Off-diagonal A blocks (stored negated) and P blocks (scaled).
+    // Off-diagonal A blocks (stored negated) and P blocks (scaled): waves 1..3
+    // take jobs pw - 1, pw + 2, ... with no branches (output pass: 16 jobs in
+    // six rounds, the two rounds past the end write the unused block 16).
     constexpr uint64_t kRow = 0x3333222110333221ull, kCol = 0x3210210100210100ull;
     constexpr int NJOBS = (MODE == kModeOut) ? 16 : 6;
+    constexpr int ROUNDS = (NJOBS + 2) / 3;
 #pragma unroll
-    for (int jj = 0; jj < 6; ++jj) {
+    for (int jj = 0; jj < ROUNDS; ++jj) {
         const int job = (pw - 1) + 3 * jj;
-        if (job < NJOBS) {
-            const int mt = (int)((kRow >> (4 * job)) & 15), nt = (int)((kCol >> (4 * job)) & 15);
-            const bool isP = job >= 6;
-            const f32x4 acc = gram_block(isP ? Q : K, K, mt, nt, g, m);
-            const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[pw][16 * mt + 4 * g]);
-            const float gc = sm.pg[pw][16 * nt + m];
-            f32x4 v;
-            if (isP) {
+        const int jt = job < NJOBS ? job : NJOBS - 1;
+        const int mt = (int)((kRow >> (4 * jt)) & 15), nt = (int)((kCol >> (4 * jt)) & 15);
+        const bool isP = jt >= 6;
+        const f32x4 acc = gram_block(isP ? Q : K, K, mt, nt, g, m);
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[pw][16 * mt + 4 * g]);
+        const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[pw][16 * mt + 4 * g]);
+        const float gc = sm.pg[pw][16 * nt + m];
+        f32x4 v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p = scale * fast_exp(gr[e] - gc) * acc[e];
-                    v[e] = (mt > nt || m <= 4 * g + e) ? p : 0.f;
-                }
-                store_block_bf16(F.P[job - 6], v, g, m);
-            } else {
-                const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[pw][16 * mt + 4 * g]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = -(br[e] * fast_exp(gr[e] - gc) * acc[e]);
-                store_block_bf16(F.An[job], v, g, m);
-            }
+        for (int e = 0; e < 4; ++e) {
+            const float x = (isP ? scale : -br[e]) * fast_exp(gr[e] - gc) * acc[e];
+            v[e] = (mt > nt || m <= 4 * g + e) ? x : 0.f;
         }
+        store_block_bf16(F.Ob[job < NJOBS ? job : 16], v, g, m);
     }
 }
 
+// 16x16x16 A operand (lane (g, m): X[m][4 g .. 4 g + 3]) of a column-major
+// block: a transpose read, lane i of group g addressing blk[4 g + i / 4][4 (i % 4)].
 __device__ __forceinline__ i16x4 lds_blk_a(const uint16_t (*blk)[TP], int g, int m) {
-    return __builtin_bit_cast(i16x4, *reinterpret_cast<const u32x2*>(&blk[m][4 * g]));
+    return lds_read_tr16(&blk[4 * g + (m >> 2)][4 * (m & 3)]);
 }
 
 __device__ __forceinline__ f32x4 mfma_x16(i16x4 a, i16x4 b, f32x4 c) {
@@ -344,12 +352,15 @@ template <bool WITH_V, bool WITH_OUT>
 __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q, const ChunkFactors& F,
                                            f32x4 (&ST)[8][2], uint32_t (&vr)[16], const uint16_t* vnext, int ncn,
                                            uint16_t* orow0, int ldv, int nc, float scale, int g, int m) {
-    // Z = K S^T
-    f32x4 X[4][2];
+    // Z = K S^T and, for the output, Y = Q S^T: one pass over the S^T operands.
+    f32x4 X[4][2], Y[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) X[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < 2; ++nt) {
+            X[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Y[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const bf16x8 sb0 = pack_acc_pair(ST[2 * kk][0], ST[2 * kk + 1][0]);
@@ -359,6 +370,11 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
             const bf16x8 a = lds_a_perm(K, RP, 16 * mt + m, kk, g);
             X[mt][0] = mfma16(a, sb0, X[mt][0]);
             X[mt][1] = mfma16(a, sb1, X[mt][1]);
+            if (WITH_OUT) {
+                const bf16x8 aq = lds_a_perm(Q, RP, 16 * mt + m, kk, g);
+                Y[mt][0] = mfma16(aq, sb0, Y[mt][0]);
+                Y[mt][1] = mfma16(aq, sb1, Y[mt][1]);
+            }
         }
     }
     // X = beta (V - Gamma Z); then the next chunk's values are requested.
@@ -393,7 +409,7 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
         f32x4 acc0 = X[b][0], acc1 = X[b][1];
 #pragma unroll
         for (int bp = 0; bp < b; ++bp) {
-            const i16x4 a = lds_blk_a(F.An[b * (b - 1) / 2 + bp], g, m);
+            const i16x4 a = lds_blk_a(F.Ob[b * (b - 1) / 2 + bp], g, m);
             acc0 = mfma_x16(a, Ub[bp][0], acc0);
             acc1 = mfma_x16(a, Ub[bp][1], acc1);
         }
@@ -414,23 +430,7 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
         }
     }
     if (WITH_OUT) {
-        // O = scale Gamma (Q S^T) + (scale P) U; S is still the chunk's entry state.
-        f32x4 Y[4][2];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) Y[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 sb0 = pack_acc_pair(ST[2 * kk][0], ST[2 * kk + 1][0]);
-            const bf16x8 sb1 = pack_acc_pair(ST[2 * kk][1], ST[2 * kk + 1][1]);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 a = lds_a_perm(Q, RP, 16 * mt + m, kk, g);
-                Y[mt][0] = mfma16(a, sb0, Y[mt][0]);
-                Y[mt][1] = mfma16(a, sb1, Y[mt][1]);
-            }
-        }
+        // O = scale Gamma (Q S^T) + (scale P) U
         uint32_t ob[4][4];   // bf16 pairs: row 16 mt + 4 g + e, columns cb + 2 m, cb + 2 m + 1
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -438,7 +438,7 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
             f32x4 y0 = Gr * Y[mt][0], y1 = Gr * Y[mt][1];
 #pragma unroll
             for (int b = 0; b <= mt; ++b) {
-                const i16x4 a = lds_blk_a(F.P[mt * (mt + 1) / 2 + b], g, m);
+                const i16x4 a = lds_blk_a(F.Ob[6 + mt * (mt + 1) / 2 + b], g, m);
                 y0 = mfma_x16(a, Ub[b][0], y0);
                 y1 = mfma_x16(a, Ub[b][1], y1);
             }
