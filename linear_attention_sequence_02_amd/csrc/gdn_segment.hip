@@ -648,53 +648,83 @@ __global__ __launch_bounds__(64 * (ChainWaves<MODE>::n + kProd)) void segment_ke
 
 // Combine, fp32: for each (sequence, V head, block of 16 state rows), walk the
 // sequence's segments: S_in(1) = H_0, S_in(j+1) = S_in(j) M_j + H_j; S_in(j) is
-// stored for pass C. Thread t: row 16 rb + t / 16, columns 8 (t % 16) .. +7.
+// stored for pass C. Each wave computes 32 of the 128 columns with fp32 MFMA
+// 16x16x4 (lane (g, m): A[m][k], B[k][m] with k = 4 kk + g; D[4 g + e][m]);
+// M_{j+1} and H_{j+1} do not depend on the recurrence and are loaded during
+// step j, so only the 16 rows of S_in pass through LDS between steps. The row
+// blocks of one (sequence, head) are consecutive in units of the head count,
+// which puts them on one XCD (blocks go round-robin to the 8 XCDs) when the
+// head count is a multiple of 8: M_j then comes from HBM once.
+__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ cu, float* __restrict__ segws,
                                                       int64_t total_tokens, int32_t num_seqs, int32_t num_v_heads,
                                                       int32_t L) {
     __shared__ float Srow[16][D + 4];
     const int tid = threadIdx.x;
-    const int rb = blockIdx.x & 7;
-    const int h = (blockIdx.x >> 3) % num_v_heads;
-    const int n = (blockIdx.x >> 3) / num_v_heads;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, g = lane >> 4, m = lane & 15;
+    const int64_t nh = (int64_t)num_seqs * num_v_heads;
+    const int64_t u = blockIdx.x % nh;
+    const int rb = (int)(blockIdx.x / nh);
+    const int h = (int)(u % num_v_heads), n = (int)(u / num_v_heads);
     const SeqRange sr = seq_range(cu, n, total_tokens);
     const int64_t nch = (sr.eos - sr.bos + kChunk - 1) / kChunk;
     const int64_t nseg = (nch + L - 1) / L;
     if (nseg < 2) return;
     const int64_t s0 = seg_base(cu, n, L);
-    const int i = tid >> 4, c0 = 8 * (tid & 15);
-    const int row = 16 * rb + i;
     auto mat = [&](int64_t jseg, int which) {
         return segws + (((size_t)(s0 + jseg) * num_v_heads + h) * kSegMats + which) * kSegMat;
     };
-    float acc[8];
-    {
-        const float* H0 = mat(0, 0) + (size_t)row * D + c0;
+    const int r0 = 16 * rb, cb = 32 * w;
+    // Lane (g, m) of tile ct: rows r0 + 4 g + e, column cb + 16 ct + m.
+    auto load_rows = [&](const float* X, f32x4 (&t)[2]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = H0[e];
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[ct][e] = X[(size_t)(r0 + 4 * g + e) * D + cb + 16 * ct + m];
+    };
+    // B operand of M: row 4 kk + g, column cb + 16 ct + m.
+    auto load_m = [&](const float* M, float (&b)[32][2]) {
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) b[kk][ct] = M[(size_t)(4 * kk + g) * D + cb + 16 * ct + m];
+    };
+    f32x4 acc[2], hn[2];
+    float bm[32][2];
+    load_rows(mat(0, 0), acc);                 // S_in(1) = H_0
+    if (nseg > 2) {
+        load_m(mat(1, 1), bm);
+        load_rows(mat(1, 0), hn);
     }
     for (int64_t jj = 1; jj < nseg; ++jj) {
-        float* Sin = mat(jj, 2) + (size_t)row * D + c0;
+        float* Sin = mat(jj, 2);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Sin[e] = acc[e];
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Sin[(size_t)(r0 + 4 * g + e) * D + cb + 16 * ct + m] = acc[ct][e];
+                Srow[4 * g + e][cb + 16 * ct + m] = acc[ct][e];
+            }
         if (jj == nseg - 1) break;
         __syncthreads();
+        // S_in(jj + 1) = S_in(jj) M_jj + H_jj
+        acc[0] = hn[0];
+        acc[1] = hn[1];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Srow[i][c0 + e] = acc[e];
-        __syncthreads();
-        const float* M = mat(jj, 1);
-        const float* H = mat(jj, 0) + (size_t)row * D + c0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = H[e];
-        for (int kk = 0; kk < D; ++kk) {
-            const float sv = Srow[i][kk];
-            const float4 m0 = *reinterpret_cast<const float4*>(M + (size_t)kk * D + c0);
-            const float4 m1 = *reinterpret_cast<const float4*>(M + (size_t)kk * D + c0 + 4);
-            acc[0] = fmaf(sv, m0.x, acc[0]); acc[1] = fmaf(sv, m0.y, acc[1]);
-            acc[2] = fmaf(sv, m0.z, acc[2]); acc[3] = fmaf(sv, m0.w, acc[3]);
-            acc[4] = fmaf(sv, m1.x, acc[4]); acc[5] = fmaf(sv, m1.y, acc[5]);
-            acc[6] = fmaf(sv, m1.z, acc[6]); acc[7] = fmaf(sv, m1.w, acc[7]);
+        for (int kk = 0; kk < 32; ++kk) {
+            const float a = Srow[m][4 * kk + g];
+            acc[0] = mfma_f32_16x16x4(a, bm[kk][0], acc[0]);
+            acc[1] = mfma_f32_16x16x4(a, bm[kk][1], acc[1]);
         }
+        if (jj + 1 < nseg - 1) {
+            load_m(mat(jj + 1, 1), bm);
+            load_rows(mat(jj + 1, 0), hn);
+        }
+        __syncthreads();
     }
 }
 
