@@ -508,43 +508,44 @@ __device__ __forceinline__ void chain_loop(SegSmem<MODE>& sm, f32x4 (&ST)[8][2],
     }
 }
 
+// One workgroup's task: segment j (of nseg) of sequence n, for V head h.
+struct SegTask {
+    SeqRange sr;
+    int64_t sg, j, nseg, c_begin, c_end, nchunks;
+    int n, h, hq;
+};
+
+struct SegArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* g;
+    const float* beta;
+    const float* initial_state;
+    float* final_state;
+    uint16_t* out;
+    float* segws;
+    int32_t num_qk_heads, num_v_heads;
+    float scale;
+};
+
 template <int MODE>
-__global__ __launch_bounds__(64 * (ChainWaves<MODE>::n + kProd)) void segment_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, const float* initial_state,
-    const int32_t* __restrict__ cu, float* final_state, uint16_t* __restrict__ out, float* __restrict__ segws,
-    int64_t total_tokens, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads, int32_t L, int64_t num_segs,
-    float scale) {
+__device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A, const SegTask& tk) {
     constexpr int NCW = ChainWaves<MODE>::n;
-    __shared__ SegSmem<MODE> sm;
+    const uint16_t* __restrict__ q = A.q;
+    const uint16_t* __restrict__ k = A.k;
+    const uint16_t* __restrict__ v = A.v;
+    const float* __restrict__ g = A.g;
+    const float* __restrict__ beta = A.beta;
+    const int32_t num_qk_heads = A.num_qk_heads, num_v_heads = A.num_v_heads;
+    const float scale = A.scale;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, lg = lane >> 4, lm = lane & 15;
-
-    // XCD-aware placement: workgroups are dealt round-robin to the 8 XCDs
-    // (bid % 8). The V heads of one (segment, QK head) - which read the same K
-    // and Q - get consecutive slots on the XCD (segment * Hqk + QK head) % 8.
-    const int group = num_v_heads / num_qk_heads;
-    const int xcd = blockIdx.x & 7;
-    const int64_t kx = blockIdx.x >> 3;
-    const int vh = (int)(kx % group);
-    const int64_t u = 8 * (kx / group) + xcd;            // (segment, QK head) unit
-    if (u >= num_segs * num_qk_heads) return;
-    const int64_t sg = u / num_qk_heads;
-    const int hq = (int)(u % num_qk_heads);
-    const int h = hq * group + vh;
-
-    const int n = find_seq_for_seg(cu, num_seqs, sg, L);
-    const SeqRange sr = seq_range(cu, n, total_tokens);
-    const int64_t j = sg - seg_base(cu, n, L);
-    const int64_t nch = (sr.eos - sr.bos + kChunk - 1) / kChunk;
-    const int64_t nseg = nch > 0 ? (nch + L - 1) / L : 1;   // an empty sequence still copies its state
-    if (j < 0 || j >= nseg) return;                          // unused segment index
-    if (MODE == kModeHM && j == nseg - 1) return;            // the last segment needs no map
-    const int64_t c_begin = j * L;
-    const int64_t c_end = (c_begin + L < nch) ? c_begin + L : nch;
-    const int64_t nchunks = c_end - c_begin;
-    float* segmat = segws + ((size_t)sg * num_v_heads + h) * kSegMats * kSegMat;
+    const SeqRange sr = tk.sr;
+    const int64_t j = tk.j, nseg = tk.nseg, c_begin = tk.c_begin, c_end = tk.c_end, nchunks = tk.nchunks;
+    const int n = tk.n, h = tk.h, hq = tk.hq;
+    float* segmat = A.segws + ((size_t)tk.sg * num_v_heads + h) * kSegMats * kSegMat;
 
     const bool producer = w >= NCW;
     const int pw = w - NCW;
@@ -605,9 +606,8 @@ __global__ __launch_bounds__(64 * (ChainWaves<MODE>::n + kProd)) void segment_ke
     {
         const float* src = nullptr;
         if (MODE == kModeOut)
-            src = (j == 0) ? (initial_state ? initial_state + ((int64_t)n * num_v_heads + h) * kSegMat : nullptr)
+            src = (j == 0) ? (A.initial_state ? A.initial_state + ((int64_t)n * num_v_heads + h) * kSegMat : nullptr)
                            : segmat + 2 * kSegMat;
-        if (MODE == kModeHM && j == 0 && initial_state) src = initial_state + ((int64_t)n * num_v_heads + h) * kSegMat;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -621,12 +621,19 @@ __global__ __launch_bounds__(64 * (ChainWaves<MODE>::n + kProd)) void segment_ke
                 SM[t][nt] = e1;
             }
     }
-    chain_loop<MODE>(sm, ST, SM, MODE == kModeHM && j > 0, v + h * D + cb, out + h * D + cb, sr.bos, sr.eos,
-                     c_begin, nchunks, ldv, scale, lg, lm);
+    chain_loop<MODE>(sm, ST, SM, MODE == kModeHM, v + h * D + cb, A.out + h * D + cb, sr.bos, sr.eos, c_begin,
+                     nchunks, ldv, scale, lg, lm);
 
     if (MODE == kModeOut) {
-        if (j == nseg - 1 && final_state) {
-            float* dst = final_state + ((int64_t)n * num_v_heads + h) * kSegMat;
+        // The last segment's end state is the sequence's final state; segment
+        // 0's (when more follow) is H_0 = S_in(1), kept for the combine.
+        float* dst = nullptr;
+        if (j == nseg - 1) {
+            if (A.final_state) dst = A.final_state + ((int64_t)n * num_v_heads + h) * kSegMat;
+        } else if (j == 0) {
+            dst = segmat;
+        }
+        if (dst) {
 #pragma unroll
             for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -640,8 +647,51 @@ __global__ __launch_bounds__(64 * (ChainWaves<MODE>::n + kProd)) void segment_ke
             for (int nt = 0; nt < 2; ++nt) {
                 const int64_t o = (int64_t)(cb + 2 * lm + nt) * D + 16 * t + 4 * lg;
                 *reinterpret_cast<f32x4*>(segmat + o) = ST[t][nt];
-                if (j > 0) *reinterpret_cast<f32x4*>(segmat + kSegMat + o) = SM[t][nt];
+                *reinterpret_cast<f32x4*>(segmat + kSegMat + o) = SM[t][nt];
             }
+    }
+}
+
+// Both launches of the segment schedule. Phase 0: segment 0 of every sequence
+// runs the output pass from the initial state (its end state is H_0), and
+// segments 1 .. nseg - 2 build their maps (H from 0, M from I). Phase 1:
+// segments >= 1 run the output pass from the combined entry states.
+__global__ __launch_bounds__(64 * (4 + kProd)) void segment_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const float* initial_state,
+    const int32_t* __restrict__ cu, float* final_state, uint16_t* __restrict__ out, float* __restrict__ segws,
+    int64_t total_tokens, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads, int32_t L, int64_t num_segs,
+    float scale, int32_t phase) {
+    __shared__ SegSmem<kModeOut> sm;
+
+    // XCD-aware placement: workgroups are dealt round-robin to the 8 XCDs
+    // (bid % 8). The V heads of one (segment, QK head) - which read the same K
+    // and Q - get consecutive slots on the XCD (segment * Hqk + QK head) % 8.
+    const int group = num_v_heads / num_qk_heads;
+    const int xcd = blockIdx.x & 7;
+    const int64_t kx = blockIdx.x >> 3;
+    const int vh = (int)(kx % group);
+    const int64_t u = 8 * (kx / group) + xcd;            // (segment, QK head) unit
+    if (u >= num_segs * num_qk_heads) return;
+    SegTask tk;
+    tk.sg = u / num_qk_heads;
+    tk.hq = (int)(u % num_qk_heads);
+    tk.h = tk.hq * group + vh;
+    tk.n = find_seq_for_seg(cu, num_seqs, tk.sg, L);
+    tk.sr = seq_range(cu, tk.n, total_tokens);
+    tk.j = tk.sg - seg_base(cu, tk.n, L);
+    const int64_t nch = (tk.sr.eos - tk.sr.bos + kChunk - 1) / kChunk;
+    tk.nseg = nch > 0 ? (nch + L - 1) / L : 1;               // an empty sequence still copies its state
+    if (tk.j < 0 || tk.j >= tk.nseg) return;                  // unused segment index
+    tk.c_begin = tk.j * L;
+    tk.c_end = (tk.c_begin + L < nch) ? tk.c_begin + L : nch;
+    tk.nchunks = tk.c_end - tk.c_begin;
+    const SegArgs A = {q, k, v, g, beta, initial_state, final_state, out, segws, num_qk_heads, num_v_heads, scale};
+    if (phase == 0) {
+        if (tk.j == 0) segment_body<kModeOut>(sm, A, tk);
+        else if (tk.j < tk.nseg - 1) segment_body<kModeHM>(*reinterpret_cast<SegSmem<kModeHM>*>(&sm), A, tk);
+    } else if (tk.j > 0) {
+        segment_body<kModeOut>(sm, A, tk);
     }
 }
 
@@ -734,13 +784,26 @@ int64_t num_segments(int64_t total_tokens, int32_t num_seqs, int L) {
 
 }  // namespace
 
-// Chunks per segment: enough segments for about 512 (segment, V head) workgroups.
+// Chunks per segment. Each of the two segment launches holds about one
+// (segment, V head) task per CU (one workgroup fits a CU): a sequence with G
+// segments contributes G - 1 tasks per V head to each launch, so G - 1 =
+// CUs / Hv segments per sequence, with enough chunks per segment to amortise
+// the map work (at least 8).
 int cp_segment_chunks(int64_t total_tokens, int32_t num_seqs, int32_t num_v_heads) {
-    const int64_t chunks = total_tokens / kChunk + num_seqs;
-    const int64_t want = (chunks * num_v_heads + 511) / 512;
-    int L = 8;
-    while (L < want && L < (1 << 24)) L <<= 1;
-    return L;
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, c = 0;
+        if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+            cus = c;
+        else
+            cus = 256;
+    }
+    const int64_t chunks = (total_tokens + kChunk - 1) / kChunk;
+    const int64_t per_head = cus / num_v_heads > 1 ? cus / num_v_heads : 1;
+    int64_t L = (chunks + per_head + num_seqs - 1) / (per_head + num_seqs);
+    if (L < 8) L = 8;
+    if (L > (1 << 24)) L = 1 << 24;
+    return (int)L;
 }
 
 size_t cp_segment_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_v_heads) {
@@ -758,25 +821,25 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const uint16_t* q = (const uint16_t*)a.q;
     const uint16_t* k = (const uint16_t*)a.k;
     const uint16_t* v = (const uint16_t*)a.v;
-    // Pass A and the combine are needed only when some sequence spans more than one segment.
-    if (a.num_seqs > 1 || a.total_tokens > (int64_t)kChunk * L) {
-        prof::begin(stream, "gdn_segment_maps");
-        hipLaunchKernelGGL((segment_kernel<kModeHM>), grid, dim3(64 * (ChainWaves<kModeHM>::n + kProd)), 0, stream, q, k, v, a.g, a.beta,
-                           a.initial_state, a.cu_seqlens, a.final_state, (uint16_t*)a.out, seg_ws, a.total_tokens,
-                           a.num_seqs, a.num_qk_heads, a.num_v_heads, L, segs, a.scale);
-        prof::end(stream);
+    // Phase 0 (segment 0's outputs and the other segments' maps) always runs;
+    // the combine and phase 1 only when some sequence spans more than one segment.
+    const bool multi = a.num_seqs > 1 || a.total_tokens > (int64_t)kChunk * L;
+    prof::begin(stream, multi ? "gdn_segment_maps" : "gdn_segment_out");
+    hipLaunchKernelGGL(segment_kernel, grid, dim3(64 * (4 + kProd)), 0, stream, q, k, v, a.g, a.beta, a.initial_state,
+                       a.cu_seqlens, a.final_state, (uint16_t*)a.out, seg_ws, a.total_tokens, a.num_seqs,
+                       a.num_qk_heads, a.num_v_heads, L, segs, a.scale, 0);
+    prof::end(stream);
+    if (multi) {
         prof::begin(stream, "gdn_segment_combine");
         hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((int64_t)a.num_seqs * a.num_v_heads * 8)), dim3(256), 0,
                            stream, a.cu_seqlens, seg_ws, a.total_tokens, a.num_seqs, a.num_v_heads, L);
         prof::end(stream);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        prof::begin(stream, "gdn_segment_out");
+        hipLaunchKernelGGL(segment_kernel, grid, dim3(64 * (4 + kProd)), 0, stream, q, k, v, a.g, a.beta,
+                           a.initial_state, a.cu_seqlens, a.final_state, (uint16_t*)a.out, seg_ws, a.total_tokens,
+                           a.num_seqs, a.num_qk_heads, a.num_v_heads, L, segs, a.scale, 1);
+        prof::end(stream);
     }
-    prof::begin(stream, "gdn_segment_out");
-    hipLaunchKernelGGL((segment_kernel<kModeOut>), grid, dim3(64 * (ChainWaves<kModeOut>::n + kProd)), 0, stream, q, k, v, a.g, a.beta,
-                       a.initial_state, a.cu_seqlens, a.final_state, (uint16_t*)a.out, seg_ws, a.total_tokens,
-                       a.num_seqs, a.num_qk_heads, a.num_v_heads, L, segs, a.scale);
-    prof::end(stream);
     return hipGetLastError();
 }
 
