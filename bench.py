@@ -8,9 +8,14 @@ with every input resident in HBM. The decode step (256 sequences x 32 heads,
 instrumentation over the timed region, on the stream the kernels run on.
 
 Roofline figures use algorithmic work only:
-  prefill: 4,194,304 flop and 24,832 bytes per token (the output pass, the
-      dominant kernel, performs this whole per-token algorithm; the segment-map
-      pass and the combine are extra work of the segment-parallel schedule)
+  prefill: 4,194,304 flop and 24,832 bytes per token. The bf16 prefill runs
+      segment-parallel in three launches: the first produces the outputs of
+      each sequence's first segment and the maps of the other segments, a
+      combine, and the output pass for segments 1 onward. The roofline object
+      is the output pass ("gdn_segment_out"), priced at 4,194,304 flop per
+      token it produces (all tokens but the first segment's, whose length
+      comes from gdn_prefill_segment_chunks); the map pass and the combine are
+      extra work of the schedule and count only in "prefill_path".
   decode: 1,080,098,816 bytes per step for 256 sequences (state read + write
       plus q, k, v, g, beta, out)
 Peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8.0 TB/s.
@@ -168,9 +173,12 @@ def main():
     log(f"[bench] prefill: {args.warmup} warmup + {args.steps} timed steps")
     ms, kern = time_calls(prefill, args.steps, args.warmup, torch)
     tokens_per_s = x.T / (ms / 1e3)
-    dom = max(kern, key=lambda k_: kern[k_][0] * kern[k_][1]) if kern else None
-    dom_ms = kern[dom][1] if dom else float("nan")
-    dom_tflops = PREFILL_FLOP_PER_TOKEN * x.T / (dom_ms / 1e3) / 1e12
+    by_time = max(kern, key=lambda k_: kern[k_][0] * kern[k_][1]) if kern else None
+    seg_chunks = gdn.gdn_prefill_segment_chunks(x.T, 1, x.hqk, x.hv, x.dk, x.dv, gdn.GDN_BF16)
+    out_tokens = x.T - min(x.T, 64 * seg_chunks) if "gdn_segment_maps" in kern else x.T
+    dom = "gdn_segment_out"
+    dom_ms = kern[dom][1] if dom in kern else float("nan")
+    dom_tflops = PREFILL_FLOP_PER_TOKEN * out_tokens / (dom_ms / 1e3) / 1e12
     path_tflops = PREFILL_FLOP_PER_TOKEN * x.T / (ms / 1e3) / 1e12
     path_gbs = PREFILL_BYTES_PER_TOKEN * x.T / (ms / 1e3) / 1e9
     workload = f"qwen3next_gdn_prefill_T{x.T}"
@@ -194,7 +202,9 @@ def main():
                    "seed": x.seed, "initial_state": "zeros"},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": dom_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": recorded_traffic(dom, workload), "ms_per_launch": dom_ms},
+                     "traffic": recorded_traffic(dom, workload), "ms_per_launch": dom_ms,
+                     "tokens_per_launch": out_tokens, "flop_per_launch": PREFILL_FLOP_PER_TOKEN * out_tokens,
+                     "longest_launch": by_time, "segment_chunks": seg_chunks},
         "prefill_path": {"tflops_algorithmic": path_tflops, "frac_mfma_peak": path_tflops / PEAK_BF16_TFLOPS,
                          "gbs_algorithmic": path_gbs, "frac_hbm_peak": path_gbs / PEAK_HBM_GBS,
                          "kernels_ms_per_launch": {k_: v_[1] for k_, v_ in kern.items()}},

@@ -68,6 +68,21 @@ size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs,
                                   int32_t d_k, int32_t d_v, gdn_dtype_t dtype);
 
 /*
+ * Planning query: chunks (of 64 tokens) per segment in the bf16 prefill's
+ * segment-parallel schedule for these sizes, as gdn_prefill will use them on
+ * the current device. Every sequence is split into segments of this many
+ * chunks (the last one shorter); the first launch produces the outputs of
+ * each sequence's first segment and the maps of the others, the last launch
+ * the outputs of segments 1 onward. For accounting and tests; the result
+ * does not need to be passed to gdn_prefill. Returns 0 for fp32 (one chain
+ * per sequence and head, no segments) and for arguments gdn_prefill would
+ * reject.
+ */
+int32_t gdn_prefill_segment_chunks(int64_t total_tokens, int32_t num_seqs,
+                                   int32_t num_qk_heads, int32_t num_v_heads,
+                                   int32_t d_k, int32_t d_v, gdn_dtype_t dtype);
+
+/*
  * Chunked prefill over packed variable-length sequences (chunk size 64: the
  * intra-chunk decay masks, the UT/WY transform of the beta-weighted
  * (I - beta k k^T) factors by a triangular solve, and the inter-chunk state

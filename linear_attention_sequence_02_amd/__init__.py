@@ -14,7 +14,8 @@ import threading
 
 import torch
 
-__all__ = ["gdn_prefill", "gdn_decode_step", "gdn_prefill_workspace_size", "gdn_status_string",
+__all__ = ["gdn_prefill", "gdn_decode_step", "gdn_prefill_workspace_size", "gdn_prefill_segment_chunks",
+           "gdn_status_string",
            "gdn_build_info", "gdn_profile_start", "gdn_profile_stop", "GDN_BF16", "GDN_FP32", "GdnError", "library_path"]
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(5)
@@ -44,6 +45,8 @@ def _load():
             lib = ctypes.CDLL(library_path)
             lib.gdn_prefill_workspace_size.restype = _sz
             lib.gdn_prefill_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, ctypes.c_int]
+            lib.gdn_prefill_segment_chunks.restype = _i32
+            lib.gdn_prefill_segment_chunks.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, ctypes.c_int]
             lib.gdn_prefill.restype = ctypes.c_int
             lib.gdn_prefill.argtypes = ([_vp] * 7 + [_i32, _i64, _i32, _i32, _i32, _i32, _f32, ctypes.c_int]
                                         + [_vp, _vp, _vp, _sz, _vp])
@@ -125,6 +128,12 @@ def _stream(stream, device):
 def gdn_prefill_workspace_size(total_tokens: int, num_seqs: int, num_qk_heads: int, num_v_heads: int,
                                d_k: int, d_v: int, dtype: int) -> int:
     return int(_load().gdn_prefill_workspace_size(total_tokens, num_seqs, num_qk_heads, num_v_heads,
+                                                  d_k, d_v, dtype))
+
+
+def gdn_prefill_segment_chunks(total_tokens: int, num_seqs: int, num_qk_heads: int, num_v_heads: int,
+                               d_k: int, d_v: int, dtype: int) -> int:
+    return int(_load().gdn_prefill_segment_chunks(total_tokens, num_seqs, num_qk_heads, num_v_heads,
                                                   d_k, d_v, dtype))
 
 

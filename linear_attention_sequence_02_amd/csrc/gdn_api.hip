@@ -35,6 +35,14 @@ size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_
     return gdn::prefill_bf16_workspace_bytes(total_tokens, num_seqs, num_qk_heads, num_v_heads);
 }
 
+int32_t gdn_prefill_segment_chunks(int64_t total_tokens, int32_t num_seqs, int32_t num_qk_heads,
+                                   int32_t num_v_heads, int32_t d_k, int32_t d_v, gdn_dtype_t dtype) {
+    if (total_tokens < 0 || num_seqs < 0) return 0;
+    if (check_heads(num_qk_heads, num_v_heads, d_k, d_v, dtype) != GDN_OK) return 0;
+    if (dtype == GDN_FP32) return 0;
+    return gdn::cp_segment_chunks(total_tokens, num_seqs, num_v_heads);
+}
+
 gdn_status_t gdn_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
                          int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k,

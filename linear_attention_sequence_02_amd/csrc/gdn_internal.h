@@ -49,6 +49,7 @@ void end(hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+int cp_segment_chunks(int64_t total_tokens, int32_t num_seqs, int32_t num_v_heads);
 size_t prefill_bf16_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_qk_heads,
                                     int32_t num_v_heads);
 

@@ -29,7 +29,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert set(declared_functions()) == {"gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step",
+    assert set(declared_functions()) == {"gdn_prefill_workspace_size", "gdn_prefill_segment_chunks", "gdn_prefill",
+                                         "gdn_decode_step",
                                          "gdn_status_string", "gdn_build_info", "gdn_profile_start",
                                          "gdn_profile_stop"}
 
@@ -57,6 +58,17 @@ def test_workspace_size(lib):
     assert ws(-1, 1, 16, 32, 128, 128, gdn.GDN_BF16) == 0
     # grows with tokens and sequences (one chunk slot per 64 tokens plus one per sequence)
     assert ws(64 * 10, 1, 16, 32, 128, 128, 0) < ws(64 * 10, 5, 16, 32, 128, 128, 0) < ws(64 * 20, 5, 16, 32, 128, 128, 0)
+
+
+def test_segment_chunks_query(lib):
+    sc = gdn.gdn_prefill_segment_chunks
+    assert sc(65536, 1, 16, 32, 128, 128, gdn.GDN_FP32) == 0
+    assert sc(65536, 1, 3, 32, 128, 128, gdn.GDN_BF16) == 0          # rejected shape
+    L = sc(65536, 1, 16, 32, 128, 128, gdn.GDN_BF16)
+    assert L >= 8
+    # enough segments per sequence for the CU count, never shorter than 8 chunks
+    assert sc(64 * 8, 1, 16, 32, 128, 128, gdn.GDN_BF16) == 8
+    assert sc(64 * 100000, 1, 16, 32, 128, 128, gdn.GDN_BF16) >= sc(65536, 1, 16, 32, 128, 128, gdn.GDN_BF16)
 
 
 def _prefill(lib, **over):
