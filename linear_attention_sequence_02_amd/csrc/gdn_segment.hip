@@ -288,29 +288,61 @@ __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFac
         return;
     }
 
-    // Off-diagonal A blocks (stored negated) and P blocks (scaled): waves 1..3
-    // take jobs pw - 1, pw + 2, ... with no branches (output pass: 16 jobs in
-    // six rounds, the two rounds past the end write the unused block 16).
-    constexpr uint64_t kRow = 0x3333222110333221ull, kCol = 0x3210210100210100ull;
-    constexpr int NJOBS = (MODE == kModeOut) ? 16 : 6;
-    constexpr int ROUNDS = (NJOBS + 2) / 3;
+    if constexpr (MODE == kModeOut) {
+        // Output pass: off-diagonal A blocks (stored negated) and P blocks
+        // (scaled). Waves 1..3 take jobs pw - 1, pw + 2, ... with no branches:
+        // 16 jobs in six rounds, the two rounds past the end write the unused
+        // block 16.
+        constexpr uint64_t kRow = 0x3333222110333221ull, kCol = 0x3210210100210100ull;
+        constexpr int NJOBS = 16;
+        constexpr int ROUNDS = (NJOBS + 2) / 3;
 #pragma unroll
-    for (int jj = 0; jj < ROUNDS; ++jj) {
-        const int job = (pw - 1) + 3 * jj;
-        const int jt = job < NJOBS ? job : NJOBS - 1;
-        const int mt = (int)((kRow >> (4 * jt)) & 15), nt = (int)((kCol >> (4 * jt)) & 15);
-        const bool isP = jt >= 6;
-        const f32x4 acc = gram_block(isP ? Q : K, K, mt, nt, g, m);
-        const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[pw][16 * mt + 4 * g]);
-        const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[pw][16 * mt + 4 * g]);
-        const float gc = sm.pg[pw][16 * nt + m];
-        f32x4 v;
+        for (int jj = 0; jj < ROUNDS; ++jj) {
+            const int job = (pw - 1) + 3 * jj;
+            const int jt = job < NJOBS ? job : NJOBS - 1;
+            const int mt = (int)((kRow >> (4 * jt)) & 15), nt = (int)((kCol >> (4 * jt)) & 15);
+            const bool isP = jt >= 6;
+            const f32x4 acc = gram_block(isP ? Q : K, K, mt, nt, g, m);
+            const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[pw][16 * mt + 4 * g]);
+            const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[pw][16 * mt + 4 * g]);
+            const float gc = sm.pg[pw][16 * nt + m];
+            f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float x = (isP ? scale : -br[e]) * fast_exp(gr[e] - gc) * acc[e];
-            v[e] = (mt > nt || m <= 4 * g + e) ? x : 0.f;
+            for (int e = 0; e < 4; ++e) {
+                const float x = (isP ? scale : -br[e]) * fast_exp(gr[e] - gc) * acc[e];
+                v[e] = (mt > nt || m <= 4 * g + e) ? x : 0.f;
+            }
+            store_block_bf16(F.Ob[job < NJOBS ? job : 16], v, g, m);
         }
-        store_block_bf16(F.Ob[job < NJOBS ? job : 16], v, g, m);
+    } else {
+        // Map pass: only the six off-diagonal A blocks (stored negated), grouped
+        // by block column so that each wave reads its K column tile once.
+        bf16x8 kc[4];
+        auto job = [&](int mt, int nt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mfma16(lds_row8(K, RP, 16 * mt + m, kk, g), kc[kk], acc);
+            const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[pw][16 * mt + 4 * g]);
+            const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[pw][16 * mt + 4 * g]);
+            const float gc = sm.pg[pw][16 * nt + m];
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = -(br[e] * fast_exp(gr[e] - gc) * acc[e]);
+            store_block_bf16(F.Ob[mt * (mt - 1) / 2 + nt], v, g, m);
+        };
+        const int nt = pw - 1;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kc[kk] = lds_row8(K, RP, 16 * nt + m, kk, g);
+        if (pw == 1) {
+            job(1, 0);
+            job(2, 0);
+            job(3, 0);
+        } else if (pw == 2) {
+            job(2, 1);
+            job(3, 1);
+        } else {
+            job(3, 2);
+        }
     }
 }
 
