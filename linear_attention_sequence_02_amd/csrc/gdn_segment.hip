@@ -393,19 +393,49 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
             X[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
             Y[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 sb0 = pack_acc_pair(ST[2 * kk][0], ST[2 * kk + 1][0]);
-        const bf16x8 sb1 = pack_acc_pair(ST[2 * kk][1], ST[2 * kk + 1][1]);
+    if constexpr (WITH_OUT) {
+        // Software-pipelined over the key steps: step kk + 1's operand rows
+        // are requested before step kk's products are issued (the scheduler
+        // alone keeps too few LDS reads in flight here).
+        bf16x8 ka[2][4], qa[2][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const bf16x8 a = lds_a_perm(K, RP, 16 * mt + m, kk, g);
-            X[mt][0] = mfma16(a, sb0, X[mt][0]);
-            X[mt][1] = mfma16(a, sb1, X[mt][1]);
-            if (WITH_OUT) {
-                const bf16x8 aq = lds_a_perm(Q, RP, 16 * mt + m, kk, g);
-                Y[mt][0] = mfma16(aq, sb0, Y[mt][0]);
-                Y[mt][1] = mfma16(aq, sb1, Y[mt][1]);
+            ka[0][mt] = lds_a_perm(K, RP, 16 * mt + m, 0, g);
+            qa[0][mt] = lds_a_perm(Q, RP, 16 * mt + m, 0, g);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int cur = kk & 1;
+            if (kk < 3) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    ka[cur ^ 1][mt] = lds_a_perm(K, RP, 16 * mt + m, kk + 1, g);
+                    qa[cur ^ 1][mt] = lds_a_perm(Q, RP, 16 * mt + m, kk + 1, g);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 sb0 = pack_acc_pair(ST[2 * kk][0], ST[2 * kk + 1][0]);
+            const bf16x8 sb1 = pack_acc_pair(ST[2 * kk][1], ST[2 * kk + 1][1]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                X[mt][0] = mfma16(ka[cur][mt], sb0, X[mt][0]);
+                X[mt][1] = mfma16(ka[cur][mt], sb1, X[mt][1]);
+                Y[mt][0] = mfma16(qa[cur][mt], sb0, Y[mt][0]);
+                Y[mt][1] = mfma16(qa[cur][mt], sb1, Y[mt][1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        // Map pass (two states held): no room for a second operand set.
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 sb0 = pack_acc_pair(ST[2 * kk][0], ST[2 * kk + 1][0]);
+            const bf16x8 sb1 = pack_acc_pair(ST[2 * kk][1], ST[2 * kk + 1][1]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8 a = lds_a_perm(K, RP, 16 * mt + m, kk, g);
+                X[mt][0] = mfma16(a, sb0, X[mt][0]);
+                X[mt][1] = mfma16(a, sb1, X[mt][1]);
             }
         }
     }
