@@ -59,6 +59,22 @@ def test_decode_step(dtype, d, n):
     _check(x, out.float().cpu().numpy().astype(np.float64), state.cpu().numpy().astype(np.float64), tol)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_decode_group3(dtype):
+    """d = 128 decode with three V heads sharing one QK head, 5 sequences (an odd head count
+    and a grouping the Qwen3-Next shape does not use)."""
+    x = I.draw(lengths=[1] * 5, hqk=1, hv=3, dk=128, dtype=dtype, seed=71, s0_std=0.3,
+               name=f"decode_{dtype}_d128_items15")
+    dev = to_device(x)
+    state = dev["s0"].clone()
+    log(f"[gpu] gdn_decode_step {x.name}")
+    import linear_attention_sequence_02_amd as gdn
+    out = gdn.gdn_decode_step(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], state, scale=x.scale)
+    torch.cuda.synchronize()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_FP32
+    _check(x, out.float().cpu().numpy().astype(np.float64), state.cpu().numpy().astype(np.float64), tol)
+
+
 # ---------------------------------------------------------------- fp32-input prefill
 
 def test_prefill_fp32_tiny():
