@@ -5,7 +5,8 @@ One step = one gdn_prefill call over the Qwen3-Next GDN layer at T = 65536
 with every input resident in HBM. The decode step (256 sequences x 32 heads,
 512 MiB fp32 state updated in place) is timed separately and reported under
 "decode". Per-kernel durations come from the library's HIP-event
-instrumentation over the timed region, on the stream the kernels run on.
+instrumentation (events around each launch, on the stream the kernels run on)
+over a second run of the same steps.
 
 Roofline figures use algorithmic work only:
   prefill: 4,194,304 flop and 24,832 bytes per token. The bf16 prefill runs
@@ -17,8 +18,17 @@ Roofline figures use algorithmic work only:
       comes from gdn_prefill_segment_chunks); the map pass and the combine are
       extra work of the schedule and count only in "prefill_path".
   decode: 1,080,098,816 bytes per step for 256 sequences (state read + write
-      plus q, k, v, g, beta, out)
+      plus q, k, v, g, beta, out); also on a state pool addressed by slot
+      ("decode.slots"), and as eager calls against graph replays, wall clock
+      per step ("decode.graph_replay", 256 and 8 sequences; a graph holds 16 steps)
 Peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8.0 TB/s.
+"step_ms" gives the mean, median and min of the prefill step (a further pass
+with events around each call). The timed run behind `value` has no
+per-kernel instrumentation; the per-kernel launch times come from a separate
+run of the same number of steps. "parity" is the rel-L2 (fp64) of the timed
+run's output, and of its final state when the oracle sample covers the
+whole input, against the fp64 oracle run for "cpu_baseline" on the same
+inputs.
 HBM traffic per launch ("traffic") comes from rocprofv3 FETCH_SIZE and
 WRITE_SIZE passes recorded in profiles/traffic.json, scaled by the same
 counters read for a plain device copy of known size (--calibration-copy); it
@@ -60,22 +70,68 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_calls(fn, steps, warmup, torch, profile=True):
+def time_calls(fn, steps, warmup, torch, profile=True, per_step=None):
+    """Mean ms per call over `steps` back-to-back calls, HIP events on the current stream around the
+    whole run and nothing else inside it (this is the number `value` comes from). If `profile`, a
+    second run of `steps` calls with the library's per-launch HIP events on gives each kernel's mean
+    launch time (the roofline's figure). If `per_step` is a list, a third run brackets each call with
+    its own events and appends the per-call times (median and min)."""
     import linear_attention_sequence_02_amd as gdn
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if profile:
-        gdn.gdn_profile_start()
     start.record(stream)
     for _ in range(steps):
         fn()
     stop.record(stream)
     torch.cuda.synchronize()
-    kernels = gdn.gdn_profile_stop() if profile else {}
-    return start.elapsed_time(stop) / steps, {k: (c, ms / c) for k, (c, ms) in kernels.items()}
+    ms = start.elapsed_time(stop) / steps
+    kernels = {}
+    if profile:
+        gdn.gdn_profile_start()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        kernels = gdn.gdn_profile_stop()
+    if per_step is not None:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per_step.extend(a.elapsed_time(b) for a, b in ev)
+    return ms, {k: (c, t / c) for k, (c, t) in kernels.items()}
+
+
+def graph_vs_eager(fn, steps, torch, per_graph=16):
+    """Microseconds per step: eager calls back to back, against replays of one HIP graph holding
+    `per_graph` consecutive calls (captured on a side stream after one warm-up call), about `steps`
+    calls of each."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            fn()
+    torch.cuda.synchronize()
+    reps = max(1, steps // per_graph)
+    res = {"calls_per_graph": per_graph}
+    for name, call, n_calls in (("eager_us_per_step", fn, reps * per_graph), ("graph_us_per_step", graph.replay, reps)):
+        call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_calls):
+            call()
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) / (reps * per_graph) * 1e6
+    return res
 
 
 def source_hash(kernel):
@@ -123,22 +179,30 @@ def cpu_baseline(x, budget_s=20.0):
     T = 512
     while True:
         t0 = time.perf_counter()
-        _, _, threads = oracle.recurrent(x.q[:T], x.k[:T], x.v[:T], x.g[:T], x.beta[:T], None, None,
-                                         scale=x.scale, return_threads=True)
+        o_ref, s_ref, threads = oracle.recurrent(x.q[:T], x.k[:T], x.v[:T], x.g[:T], x.beta[:T], None, None,
+                                                 scale=x.scale, return_threads=True)
         dt = time.perf_counter() - t0
         if dt >= budget_s / 4 or T >= x.T:
             break
         T = min(x.T, int(T * max(2.0, budget_s / 4 / max(dt, 1e-3))))
-    return {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    base = {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {T} of {x.T} tokens of the same input, all {x.hv} V heads, fp64 recurrence, "
                       f"{dt:.1f} s"}
+    return base, T, o_ref, (s_ref if T == x.T else None)
+
+
+def rel_l2(a, ref):
+    """||a - ref||_2 / ||ref||_2 in fp64."""
+    a = np.asarray(a, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm((a - ref).ravel()) / np.linalg.norm(ref.ravel()))
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--T", type=int, default=65536)
     ap.add_argument("--decode-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -171,7 +235,8 @@ def main():
                         workspace=ws)
 
     log(f"[bench] prefill: {args.warmup} warmup + {args.steps} timed steps")
-    ms, kern = time_calls(prefill, args.steps, args.warmup, torch)
+    each = []
+    ms, kern = time_calls(prefill, args.steps, args.warmup, torch, per_step=each)
     tokens_per_s = x.T / (ms / 1e3)
     by_time = max(kern, key=lambda k_: kern[k_][0] * kern[k_][1]) if kern else None
     seg_chunks = gdn.gdn_prefill_segment_chunks(x.T, 1, x.hqk, x.hv, x.dk, x.dv, gdn.GDN_BF16)
@@ -205,10 +270,14 @@ def main():
                      "traffic": recorded_traffic(dom, workload), "ms_per_launch": dom_ms,
                      "tokens_per_launch": out_tokens, "flop_per_launch": PREFILL_FLOP_PER_TOKEN * out_tokens,
                      "longest_launch": by_time, "segment_chunks": seg_chunks},
+        "step_ms": {"mean": ms, "median": float(np.median(each)), "min": float(np.min(each)),
+                    "n": len(each)},
         "prefill_path": {"tflops_algorithmic": path_tflops, "frac_mfma_peak": path_tflops / PEAK_BF16_TFLOPS,
                          "gbs_algorithmic": path_gbs, "frac_hbm_peak": path_gbs / PEAK_HBM_GBS,
                          "kernels_ms_per_launch": {k_: v_[1] for k_, v_ in kern.items()}},
     }
+    out_host = out.view(torch.int16).cpu().numpy()
+    fin_host = fin.cpu().numpy()
     del d, out, fin, ws
     torch.cuda.empty_cache()
 
@@ -234,7 +303,39 @@ def main():
                                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                                          "traffic": recorded_traffic("gdn_decode_step", f"qwen3next_gdn_decode_N{n}")}}
         log(f"[bench] decode {dms:.3f} ms/step, {gbs:.1f} GB/s")
-        del dd, state, dout
+
+        # The same step on a state pool: the 256 sequences' states are 256 scattered rows of a
+        # 384-row pool (seeded choice), addressed by slot index.
+        slots = 384
+        pool = torch.zeros((slots,) + tuple(dd["s0"].shape[1:]), dtype=torch.float32, device=dev)
+        idx = torch.from_numpy(np.random.default_rng(7).choice(slots, size=n, replace=False).astype(np.int32)).to(dev)
+        pool[idx.long()] = dd["s0"]
+
+        def decode_slots():
+            gdn.gdn_decode_step_slots(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], pool, idx, out=dout)
+
+        sms, skern = time_calls(decode_slots, args.steps, args.warmup, torch)
+        skms = skern.get("gdn_decode_step", (0, sms))[1]
+        result["decode"]["slots"] = {"pool_slots": slots, "ms_per_step": sms, "kernel_ms_per_launch": skms,
+                                     "GB_per_s": nbytes / (skms / 1e3) / 1e9,
+                                     "frac_hbm_peak": nbytes / (skms / 1e3) / 1e9 / PEAK_HBM_GBS}
+        log(f"[bench] decode on a state pool {sms:.3f} ms/step")
+        result["decode"]["graph_replay"] = {f"N{n}": graph_vs_eager(decode_slots, args.steps, torch)}
+        del dd, state, dout, pool, idx
+        torch.cuda.empty_cache()
+
+        # Launch overhead: a small batch (8 sequences), eager calls against replays of a captured graph.
+        y8 = I.decode_batch(8)
+        d8 = to_device(y8, dev)
+        st8 = d8["s0"].clone()
+        o8 = torch.empty_like(d8["v"])
+
+        def decode8():
+            gdn.gdn_decode_step(d8["q"], d8["k"], d8["v"], d8["g"], d8["beta"], st8, out=o8)
+
+        result["decode"]["graph_replay"]["N8"] = graph_vs_eager(decode8, args.steps, torch)
+        log(f"[bench] decode graph replay {result['decode']['graph_replay']}")
+        del d8, st8, o8
 
     if args.calibration_copy:
         a_ = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -247,7 +348,13 @@ def main():
 
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle on host cores)")
-        result["cpu_baseline"] = cpu_baseline(x)
+        base, Tref, o_ref, s_ref = cpu_baseline(x)
+        result["cpu_baseline"] = base
+        # The timed run's own output against the oracle's (the same inputs): rel-L2 in fp64.
+        o_gpu = (out_host[:Tref].astype(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        result["parity"] = {"tokens_compared": Tref, "out_rel_l2": rel_l2(o_gpu, o_ref),
+                            "state_rel_l2": None if s_ref is None else rel_l2(fin_host, s_ref),
+                            "tolerance": 1e-2}
     print(json.dumps(result), flush=True)
 
 

@@ -137,6 +137,52 @@ gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v,
                              void* out, void* stream);
 
 /*
+ * State-pool variants (page "Qwen3-Next and vLLM: Advancing Efficient
+ * Long-Context AI with Hybrid Architecture": section "Hybrid Attention: The
+ * Best of Both Worlds" names the hybrid cache manager that keeps each
+ * request's linear-attention state, section "Performance Optimized for Real
+ * Applications" the full graph mode of decode). The states live in a pool
+ * indexed by slot instead of one row per sequence of the batch:
+ *
+ *   state_pool     [num_slots, num_v_heads, d_v, d_k] float, device
+ *   state_indices  [num_seqs] int32, device: sequence n reads and writes pool
+ *                  row state_indices[n]. An index outside [0, num_slots) marks
+ *                  a padding entry: no pool row is read or written for it (the
+ *                  kernels check the range; it is not an error). Non-padding
+ *                  indices must be distinct; sharing a row is undefined.
+ * Rows not named by an index are never touched. Everything else is as in
+ * gdn_decode_step / gdn_prefill, including the argument checks and the
+ * statuses; num_slots < 0 or a NULL state_indices (with num_seqs > 0), or a
+ * NULL state_pool with num_slots > 0, is GDN_ERR_INVALID_ARG.
+ */
+
+/*
+ * Decode step on a state pool. A padding entry's outputs are written as zeros.
+ */
+gdn_status_t gdn_decode_step_slots(const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta,
+                                   float* state_pool, const int32_t* state_indices, int32_t num_slots,
+                                   int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads,
+                                   int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype,
+                                   void* out, void* stream);
+
+/*
+ * Prefill on a state pool: sequence n starts from pool row state_indices[n]
+ * when has_initial_state is NULL or has_initial_state[n] != 0 (device int32
+ * [num_seqs]), from zeros otherwise, and its final state is written back to
+ * the same row. A padding entry starts from zeros, its outputs are computed,
+ * and no row is written. Workspace as for gdn_prefill with the same sizes.
+ */
+gdn_status_t gdn_prefill_slots(const void* q, const void* k, const void* v,
+                               const float* g, const float* beta,
+                               float* state_pool, const int32_t* state_indices,
+                               const int32_t* has_initial_state, int32_t num_slots,
+                               const int32_t* cu_seqlens, int32_t num_seqs,
+                               int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads,
+                               int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype,
+                               void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Instrumentation (for benchmarks and profiling; process-global, not
  * thread-safe, not for graph capture). After gdn_profile_start(), every kernel
  * the library launches is bracketed by a pair of HIP events recorded on the

@@ -14,7 +14,8 @@ import threading
 
 import torch
 
-__all__ = ["gdn_prefill", "gdn_decode_step", "gdn_prefill_workspace_size", "gdn_prefill_segment_chunks",
+__all__ = ["gdn_prefill", "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots",
+           "gdn_prefill_workspace_size", "gdn_prefill_segment_chunks",
            "gdn_status_string",
            "gdn_build_info", "gdn_profile_start", "gdn_profile_stop", "GDN_BF16", "GDN_FP32", "GdnError", "library_path"]
 
@@ -52,6 +53,11 @@ def _load():
                                         + [_vp, _vp, _vp, _sz, _vp])
             lib.gdn_decode_step.restype = ctypes.c_int
             lib.gdn_decode_step.argtypes = [_vp] * 6 + [_i32] * 5 + [_f32, ctypes.c_int, _vp, _vp]
+            lib.gdn_decode_step_slots.restype = ctypes.c_int
+            lib.gdn_decode_step_slots.argtypes = [_vp] * 7 + [_i32] * 6 + [_f32, ctypes.c_int, _vp, _vp]
+            lib.gdn_prefill_slots.restype = ctypes.c_int
+            lib.gdn_prefill_slots.argtypes = ([_vp] * 8 + [_i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
+                                                          ctypes.c_int, _vp, _vp, _sz, _vp])
             lib.gdn_status_string.restype = ctypes.c_char_p
             lib.gdn_status_string.argtypes = [ctypes.c_int]
             lib.gdn_build_info.restype = ctypes.c_char_p
@@ -193,4 +199,64 @@ def gdn_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, out=None, st
                                  dk, dv, float(scale), dt, _ptr(out), _stream(stream, dev))
     if st != GDN_OK:
         raise GdnError(st, "gdn_decode_step")
+    return out
+
+
+def gdn_decode_step_slots(q, k, v, g, beta, state_pool, state_indices, *, scale: float = 1.0, out=None,
+                          stream=None):
+    """One decode step on a state pool [S, Hv, d, d] fp32: sequence n updates row state_indices[n]
+    (int32 [N] on the device; an index outside [0, S) is a padding entry with zero outputs).
+    Returns out [N, Hv, d]."""
+    dev = q.device
+    _check(q, "q", device=dev)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, q.dtype, dev)
+    for name, t in (("g", g), ("beta", beta), ("state_pool", state_pool)):
+        _check(t, name, torch.float32, dev)
+    _check(state_indices, "state_indices", torch.int32, dev)
+    N, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    if out is None:
+        out = torch.empty((N, hv, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", q.dtype, dev)
+    st = _load().gdn_decode_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                                       _ptr(state_indices), state_pool.shape[0], N, hqk, hv, dk, dv,
+                                       float(scale), dt, _ptr(out), _stream(stream, dev))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_decode_step_slots")
+    return out
+
+
+def gdn_prefill_slots(q, k, v, g, beta, state_pool, state_indices, has_initial_state=None, cu_seqlens=None, *,
+                      scale: float = 1.0, out=None, workspace=None, stream=None):
+    """Chunked prefill on a state pool [S, Hv, d, d] fp32: sequence n starts from row state_indices[n]
+    (from zeros where has_initial_state[n] == 0) and writes its final state back to that row.
+    state_indices and has_initial_state are int32 [N] on the device. Returns out."""
+    dev = q.device
+    _check(q, "q", device=dev)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, q.dtype, dev)
+    for name, t in (("g", g), ("beta", beta), ("state_pool", state_pool)):
+        _check(t, name, torch.float32, dev)
+    for name, t in (("state_indices", state_indices), ("has_initial_state", has_initial_state),
+                    ("cu_seqlens", cu_seqlens)):
+        _check(t, name, torch.int32, dev)
+    T, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    n = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    if out is None:
+        out = torch.empty((T, hv, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", q.dtype, dev)
+    need = gdn_prefill_workspace_size(T, n, hqk, hv, dk, dv, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _load().gdn_prefill_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                                   _ptr(state_indices), _ptr(has_initial_state), state_pool.shape[0],
+                                   _ptr(cu_seqlens), n, T, hqk, hv, dk, dv, float(scale), dt, _ptr(out),
+                                   _ptr(workspace), ws_bytes, _stream(stream, dev))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_prefill_slots")
     return out

@@ -43,11 +43,17 @@ int32_t gdn_prefill_segment_chunks(int64_t total_tokens, int32_t num_seqs, int32
     return gdn::cp_segment_chunks(total_tokens, num_seqs, num_v_heads);
 }
 
-gdn_status_t gdn_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                         const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
-                         int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k,
-                         int32_t d_v, float scale, gdn_dtype_t dtype, void* out, float* final_state,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of gdn_prefill and gdn_prefill_slots.
+gdn_status_t prefill_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                          int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k,
+                          int32_t d_v, float scale, gdn_dtype_t dtype, void* out, float* final_state,
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          const int32_t* state_indices, const int32_t* has_initial, int32_t num_slots) {
     gdn_status_t st = check_heads(num_qk_heads, num_v_heads, d_k, d_v, dtype);
     if (st != GDN_OK) return st;
     if (total_tokens < 0 || num_seqs < 0) return GDN_ERR_INVALID_ARG;
@@ -63,6 +69,7 @@ gdn_status_t gdn_prefill(const void* q, const void* k, const void* v, const floa
     gdn::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.initial_state = initial_state; a.cu_seqlens = cu_seqlens; a.final_state = final_state;
+    a.state_indices = state_indices; a.has_initial = has_initial; a.num_slots = num_slots;
     a.out = out; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.total_tokens = total_tokens; a.num_seqs = num_seqs; a.num_qk_heads = num_qk_heads;
     a.num_v_heads = num_v_heads; a.d = d_k; a.scale = scale; a.bf16 = (dtype == GDN_BF16);
@@ -70,23 +77,74 @@ gdn_status_t gdn_prefill(const void* q, const void* k, const void* v, const floa
     return hip_status(a.bf16 ? gdn::launch_prefill_bf16(a, s) : gdn::launch_prefill_f32(a, s));
 }
 
-gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                             float* state, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads,
-                             int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype, void* out,
-                             void* stream) {
+// Shared body of gdn_decode_step and gdn_decode_step_slots.
+gdn_status_t decode_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         float* state, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads,
+                         int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype, void* out, void* stream,
+                         const int32_t* state_indices, int32_t num_slots) {
     if (num_qk_heads <= 0 || num_v_heads <= 0 || d_k <= 0 || d_v <= 0 || num_seqs < 0)
         return GDN_ERR_INVALID_ARG;
     if (num_v_heads % num_qk_heads != 0) return GDN_ERR_INVALID_ARG;
     if (dtype != GDN_BF16 && dtype != GDN_FP32) return GDN_ERR_INVALID_ARG;
     if (d_k != d_v || !fp32_head_size_ok(d_k)) return GDN_ERR_UNSUPPORTED;
     if (num_seqs == 0) return GDN_OK;
-    if (!q || !k || !v || !g || !beta || !state || !out) return GDN_ERR_INVALID_ARG;
+    if (!q || !k || !v || !g || !beta || !out) return GDN_ERR_INVALID_ARG;
+    if (!state && !(state_indices && num_slots == 0)) return GDN_ERR_INVALID_ARG;
     if ((int64_t)num_seqs * num_v_heads > INT32_MAX) return GDN_ERR_UNSUPPORTED;
     gdn::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.out = out;
+    a.state_indices = state_indices; a.num_slots = num_slots;
     a.num_seqs = num_seqs; a.num_qk_heads = num_qk_heads; a.num_v_heads = num_v_heads; a.d = d_k;
     a.scale = scale; a.bf16 = (dtype == GDN_BF16);
     return hip_status(gdn::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status_t gdn_prefill(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                         const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                         int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k,
+                         int32_t d_v, float scale, gdn_dtype_t dtype, void* out, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, num_qk_heads,
+                        num_v_heads, d_k, d_v, scale, dtype, out, final_state, workspace, workspace_bytes, stream,
+                        nullptr, nullptr, 0);
+}
+
+gdn_status_t gdn_prefill_slots(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                               float* state_pool, const int32_t* state_indices, const int32_t* has_initial_state,
+                               int32_t num_slots, const int32_t* cu_seqlens, int32_t num_seqs,
+                               int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k,
+                               int32_t d_v, float scale, gdn_dtype_t dtype, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (num_slots < 0) return GDN_ERR_INVALID_ARG;
+    if (num_seqs > 0 && state_indices == nullptr) return GDN_ERR_INVALID_ARG;
+    if (num_slots > 0 && state_pool == nullptr) return GDN_ERR_INVALID_ARG;
+    return prefill_impl(q, k, v, g, beta, state_pool, cu_seqlens, num_seqs, total_tokens, num_qk_heads,
+                        num_v_heads, d_k, d_v, scale, dtype, out, state_pool, workspace, workspace_bytes, stream,
+                        state_indices, has_initial_state, num_slots);
+}
+
+gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                             float* state, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads,
+                             int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype, void* out,
+                             void* stream) {
+    if (num_seqs > 0 && state == nullptr) return GDN_ERR_INVALID_ARG;
+    return decode_impl(q, k, v, g, beta, state, num_seqs, num_qk_heads, num_v_heads, d_k, d_v, scale, dtype, out,
+                       stream, nullptr, 0);
+}
+
+gdn_status_t gdn_decode_step_slots(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                                   float* state_pool, const int32_t* state_indices, int32_t num_slots,
+                                   int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k,
+                                   int32_t d_v, float scale, gdn_dtype_t dtype, void* out, void* stream) {
+    if (num_slots < 0) return GDN_ERR_INVALID_ARG;
+    if (num_seqs > 0 && state_indices == nullptr) return GDN_ERR_INVALID_ARG;
+    if (num_slots > 0 && state_pool == nullptr) return GDN_ERR_INVALID_ARG;
+    return decode_impl(q, k, v, g, beta, state_pool, num_seqs, num_qk_heads, num_v_heads, d_k, d_v, scale, dtype,
+                       out, stream, state_indices, num_slots);
 }
 
 const char* gdn_status_string(gdn_status_t s) {

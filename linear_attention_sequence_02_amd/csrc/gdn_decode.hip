@@ -10,6 +10,10 @@
 // second pass over the state. Rows of S are independent: every row i needs
 // only its own dot products a_i, b_i.
 //
+// With a state pool, sequence n's state is row state_indices[n] of the pool;
+// an index outside the pool marks a padding entry (state untouched, zero
+// outputs).
+//
 // Memory pattern: the state is >99% of the bytes (64 KiB per head at d = 128).
 // Each thread owns R rows x 16 columns as four dwordx4 loads per row; the L
 // lanes that share a row are adjacent, so one load instruction of a wave
@@ -33,7 +37,8 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(512) void decode_step_kernel(
     const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-    int32_t num_qk_heads, int32_t num_v_heads, float scale, void* __restrict__ out_) {
+    int32_t num_qk_heads, int32_t num_v_heads, float scale, void* __restrict__ out_,
+    const int32_t* __restrict__ state_indices, int32_t num_slots) {
     constexpr int L = D / 16;                    // lanes per state row (16 floats each)
     constexpr int NT = (D * L < 512) ? D * L : 512;
     constexpr int ROWS_PER_PASS = NT / L;
@@ -47,8 +52,22 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
     const int n = static_cast<int>(sh / num_v_heads);
     const int h = static_cast<int>(sh % num_v_heads);
     const int hq = h / (num_v_heads / num_qk_heads);
+    const int64_t vo_base = sh * D;
 
-    f32x4* S = reinterpret_cast<f32x4*>(state + sh * (int64_t)D * D);
+    // Padding entry of a slot-indexed batch: no state access, zero outputs.
+    const int64_t srow = state_row(state_indices, num_slots, n);
+    if (srow < 0) {
+        if (c == 0) {
+#pragma unroll
+            for (int m = 0; m < R; ++m) {
+                const int row = r0 + m * ROWS_PER_PASS;
+                if constexpr (BF16) reinterpret_cast<uint16_t*>(out_)[vo_base + row] = 0;
+                else reinterpret_cast<float*>(out_)[vo_base + row] = 0.f;
+            }
+        }
+        return;
+    }
+    f32x4* S = reinterpret_cast<f32x4*>(state + (srow * num_v_heads + h) * (int64_t)D * D);
 
     // Issue the state loads first: R rows x 4 float4 per thread.
     f32x4 s[R][4];
@@ -94,7 +113,6 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
         for (int e = 0; e < 4; ++e) kq = fmaf(kr[i][e], qr[i][e], kq);
     kq = group_sum<L>(kq);
 
-    const int64_t vo_base = sh * D;
 #pragma unroll
     for (int m = 0; m < R; ++m) {
         const int row = r0 + m * ROWS_PER_PASS;
@@ -135,7 +153,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.num_seqs * a.num_v_heads;
     prof::begin(stream, "gdn_decode_step");
     hipLaunchKernelGGL((decode_step_kernel<D, BF16>), dim3((unsigned)blocks), dim3(NT), 0, stream,
-                       a.q, a.k, a.v, a.g, a.beta, a.state, a.num_qk_heads, a.num_v_heads, a.scale, a.out);
+                       a.q, a.k, a.v, a.g, a.beta, a.state, a.num_qk_heads, a.num_v_heads, a.scale, a.out,
+                       a.state_indices, a.num_slots);
     prof::end(stream);
     return hipGetLastError();
 }

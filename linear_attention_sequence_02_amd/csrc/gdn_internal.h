@@ -17,6 +17,8 @@ struct DecodeArgs {
     const float* beta;
     float* state;
     void* out;
+    const int32_t* state_indices;   // null: sequence n uses state row n; else row state_indices[n]
+    int32_t num_slots;              // rows in the state pool (with state_indices)
     int32_t num_seqs, num_qk_heads, num_v_heads, d;
     float scale;
     bool bf16;
@@ -31,6 +33,9 @@ struct PrefillArgs {
     const float* initial_state;   // may be null (zeros)
     const int32_t* cu_seqlens;    // may be null (one sequence of total_tokens)
     float* final_state;           // may be null
+    const int32_t* state_indices; // null: sequence n uses state row n; else row state_indices[n]
+    const int32_t* has_initial;   // null: every sequence reads its initial state row (if any)
+    int32_t num_slots;            // rows in the state pool (with state_indices)
     void* out;
     void* workspace;
     size_t workspace_bytes;
@@ -39,6 +44,15 @@ struct PrefillArgs {
     float scale;
     bool bf16;
 };
+
+// Row of the state array that sequence n reads and writes: n itself, or its
+// slot in a state pool. A slot outside [0, num_slots) marks a padding entry
+// (-1): no state is read or written for it.
+__device__ __forceinline__ int64_t state_row(const int32_t* state_indices, int32_t num_slots, int n) {
+    if (state_indices == nullptr) return n;
+    const int32_t s = state_indices[n];
+    return (s >= 0 && s < num_slots) ? s : -1;
+}
 
 namespace prof {
 // Event pair around one kernel launch when instrumentation is on (no-op otherwise).

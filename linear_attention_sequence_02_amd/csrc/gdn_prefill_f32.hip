@@ -42,7 +42,8 @@ __global__ __launch_bounds__(2 * D) void prefill_f32_kernel(
     const float* __restrict__ g, const float* __restrict__ beta,
     const float* initial_state, const int32_t* __restrict__ cu_seqlens, float* final_state,
     float* __restrict__ out, int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads,
-    float scale) {
+    float scale, const int32_t* __restrict__ state_indices, const int32_t* __restrict__ has_initial,
+    int32_t num_slots) {
     constexpr int NT = 2 * D;
     constexpr int H = D / 2;   // key columns per thread
     __shared__ F32Smem<D> sm;
@@ -57,10 +58,14 @@ __global__ __launch_bounds__(2 * D) void prefill_f32_kernel(
     const int64_t bos = cu_seqlens ? (int64_t)cu_seqlens[n] : 0;
     const int64_t eos = cu_seqlens ? (int64_t)cu_seqlens[n + 1] : total_tokens;
 
+    // State row of this sequence (a pool slot, or -1 for a padding entry: zero
+    // entry state, nothing written back).
+    const int64_t srow = state_row(state_indices, num_slots, n);
+    const bool read_init = initial_state && srow >= 0 && (has_initial == nullptr || has_initial[n] != 0);
     float s[H];
-    const int64_t sbase = (((int64_t)n * num_v_heads + h) * D + i) * D + jb;
+    const int64_t sbase = ((srow * num_v_heads + h) * D + i) * D + jb;
 #pragma unroll
-    for (int jj = 0; jj < H; ++jj) s[jj] = initial_state ? initial_state[sbase + jj] : 0.f;
+    for (int jj = 0; jj < H; ++jj) s[jj] = read_init ? initial_state[sbase + jj] : 0.f;
 
     for (int64_t c0 = bos; c0 < eos; c0 += kChunk) {
         const int nc = (int)((eos - c0) < kChunk ? (eos - c0) : kChunk);
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(2 * D) void prefill_f32_kernel(
         }
         __syncthreads();
     }
-    if (final_state) {
+    if (final_state && srow >= 0) {
 #pragma unroll
         for (int jj = 0; jj < H; ++jj) final_state[sbase + jj] = s[jj];
     }
@@ -178,7 +183,7 @@ static hipError_t launch_f32_t(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3((unsigned)blocks), dim3(2 * D), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, a.g, a.beta,
                        a.initial_state, a.cu_seqlens, a.final_state, (float*)a.out, a.total_tokens,
-                       a.num_qk_heads, a.num_v_heads, a.scale);
+                       a.num_qk_heads, a.num_v_heads, a.scale, a.state_indices, a.has_initial, a.num_slots);
     prof::end(stream);
     return hipGetLastError();
 }

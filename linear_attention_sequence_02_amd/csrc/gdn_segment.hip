@@ -587,6 +587,9 @@ struct SegArgs {
     float* final_state;
     uint16_t* out;
     float* segws;
+    const int32_t* state_indices;   // null: sequence n's state row is n
+    const int32_t* has_initial;     // null: read the entry state whenever initial_state is given
+    int32_t num_slots;
     int32_t num_qk_heads, num_v_heads;
     float scale;
 };
@@ -667,9 +670,17 @@ __device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A
     f32x4 ST[8][2], SM[8][2];
     {
         const float* src = nullptr;
-        if (MODE == kModeOut)
-            src = (j == 0) ? (A.initial_state ? A.initial_state + ((int64_t)n * num_v_heads + h) * kSegMat : nullptr)
-                           : segmat + 2 * kSegMat;
+        if (MODE == kModeOut) {
+            if (j == 0) {
+                // Entry state: the sequence's state row (a pool slot; none for a
+                // padding entry, or when the sequence starts from zeros).
+                const int64_t srow = state_row(A.state_indices, A.num_slots, n);
+                if (A.initial_state && srow >= 0 && (A.has_initial == nullptr || A.has_initial[n] != 0))
+                    src = A.initial_state + (srow * num_v_heads + h) * kSegMat;
+            } else {
+                src = segmat + 2 * kSegMat;
+            }
+        }
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -691,7 +702,8 @@ __device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A
         // 0's (when more follow) is H_0 = S_in(1), kept for the combine.
         float* dst = nullptr;
         if (j == nseg - 1) {
-            if (A.final_state) dst = A.final_state + ((int64_t)n * num_v_heads + h) * kSegMat;
+            const int64_t srow = state_row(A.state_indices, A.num_slots, n);
+            if (A.final_state && srow >= 0) dst = A.final_state + (srow * num_v_heads + h) * kSegMat;
         } else if (j == 0) {
             dst = segmat;
         }
@@ -723,7 +735,7 @@ __global__ __launch_bounds__(64 * (4 + kProd)) void segment_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, const float* initial_state,
     const int32_t* __restrict__ cu, float* final_state, uint16_t* __restrict__ out, float* __restrict__ segws,
     int64_t total_tokens, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads, int32_t L, int64_t num_segs,
-    float scale, int32_t phase) {
+    float scale, int32_t phase, const int32_t* state_indices, const int32_t* has_initial, int32_t num_slots) {
     __shared__ SegSmem<kModeOut> sm;
 
     // XCD-aware placement: workgroups are dealt round-robin to the 8 XCDs
@@ -748,7 +760,8 @@ __global__ __launch_bounds__(64 * (4 + kProd)) void segment_kernel(
     tk.c_begin = tk.j * L;
     tk.c_end = (tk.c_begin + L < nch) ? tk.c_begin + L : nch;
     tk.nchunks = tk.c_end - tk.c_begin;
-    const SegArgs A = {q, k, v, g, beta, initial_state, final_state, out, segws, num_qk_heads, num_v_heads, scale};
+    const SegArgs A = {q, k, v, g, beta, initial_state, final_state, out, segws, state_indices, has_initial,
+                       num_slots, num_qk_heads, num_v_heads, scale};
     if (phase == 0) {
         if (tk.j == 0) segment_body<kModeOut>(sm, A, tk);
         else if (tk.j < tk.nseg - 1) segment_body<kModeHM>(*reinterpret_cast<SegSmem<kModeHM>*>(&sm), A, tk);
@@ -889,7 +902,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     prof::begin(stream, multi ? "gdn_segment_maps" : "gdn_segment_out");
     hipLaunchKernelGGL(segment_kernel, grid, dim3(64 * (4 + kProd)), 0, stream, q, k, v, a.g, a.beta, a.initial_state,
                        a.cu_seqlens, a.final_state, (uint16_t*)a.out, seg_ws, a.total_tokens, a.num_seqs,
-                       a.num_qk_heads, a.num_v_heads, L, segs, a.scale, 0);
+                       a.num_qk_heads, a.num_v_heads, L, segs, a.scale, 0, a.state_indices, a.has_initial,
+                       a.num_slots);
     prof::end(stream);
     if (multi) {
         prof::begin(stream, "gdn_segment_combine");
@@ -899,7 +913,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
         prof::begin(stream, "gdn_segment_out");
         hipLaunchKernelGGL(segment_kernel, grid, dim3(64 * (4 + kProd)), 0, stream, q, k, v, a.g, a.beta,
                            a.initial_state, a.cu_seqlens, a.final_state, (uint16_t*)a.out, seg_ws, a.total_tokens,
-                           a.num_seqs, a.num_qk_heads, a.num_v_heads, L, segs, a.scale, 1);
+                           a.num_seqs, a.num_qk_heads, a.num_v_heads, L, segs, a.scale, 1, a.state_indices,
+                           a.has_initial, a.num_slots);
         prof::end(stream);
     }
     return hipGetLastError();

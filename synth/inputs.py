@@ -257,3 +257,10 @@ def as_f32(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def chunk_count(lengths, chunk: int = 64) -> int:
     return int(sum(math.ceil(L / chunk) for L in lengths))
+
+
+def state_pool(num_slots: int, hv: int, d: int, seed: int, std: float = 0.3) -> np.ndarray:
+    """A state pool [num_slots, hv, d, d] fp32 = std * N(0, 1) from default_rng(seed) (the per-request
+    states a serving cache holds, addressed by slot)."""
+    rng = np.random.default_rng(seed)
+    return (std * rng.standard_normal((num_slots, hv, d, d))).astype(np.float32)

@@ -30,7 +30,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert set(declared_functions()) == {"gdn_prefill_workspace_size", "gdn_prefill_segment_chunks", "gdn_prefill",
-                                         "gdn_decode_step",
+                                         "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots",
                                          "gdn_status_string", "gdn_build_info", "gdn_profile_start",
                                          "gdn_profile_stop"}
 
@@ -128,6 +128,54 @@ def test_decode_rejects(lib, over, status):
 
 def test_decode_with_no_sequences_is_a_no_op(lib):
     assert _decode(lib, n=0) == gdn.GDN_OK
+
+
+def _decode_slots(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, pool=FAKE, idx=FAKE, slots=8, n=4, hqk=16, hv=32, dk=128,
+             dv=128, scale=1.0, dt=gdn.GDN_BF16, out=FAKE, stream=None)
+    a.update(over)
+    return lib.gdn_decode_step_slots(a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["idx"], a["slots"],
+                                     a["n"], a["hqk"], a["hv"], a["dk"], a["dv"], a["scale"], a["dt"], a["out"],
+                                     a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(slots=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(idx=None), gdn.GDN_ERR_INVALID_ARG),              # indices are required with sequences
+    (dict(pool=None), gdn.GDN_ERR_INVALID_ARG),             # a non-empty pool needs its pointer
+    (dict(hqk=5), gdn.GDN_ERR_INVALID_ARG),
+    (dict(out=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dk=100, dv=100), gdn.GDN_ERR_UNSUPPORTED),
+])
+def test_decode_slots_rejects(lib, over, status):
+    assert _decode_slots(lib, **over) == status
+
+
+def test_decode_slots_with_no_sequences_is_a_no_op(lib):
+    assert _decode_slots(lib, n=0, idx=None) == gdn.GDN_OK
+
+
+def _prefill_slots(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, pool=FAKE, idx=FAKE, has=None, slots=8, cu=FAKE, n=2,
+             T=100, hqk=16, hv=32, dk=128, dv=128, scale=1.0, dt=gdn.GDN_BF16, out=FAKE, ws=FAKE, wsb=1 << 40,
+             stream=None)
+    a.update(over)
+    return lib.gdn_prefill_slots(a["q"], a["k"], a["v"], a["g"], a["beta"], a["pool"], a["idx"], a["has"],
+                                 a["slots"], a["cu"], a["n"], a["T"], a["hqk"], a["hv"], a["dk"], a["dv"],
+                                 a["scale"], a["dt"], a["out"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(slots=-2), gdn.GDN_ERR_INVALID_ARG),
+    (dict(idx=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(pool=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(hqk=3), gdn.GDN_ERR_INVALID_ARG),
+    (dict(cu=None, n=2), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dk=64, dv=64), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(ws=None), gdn.GDN_ERR_WORKSPACE),
+])
+def test_prefill_slots_rejects(lib, over, status):
+    assert _prefill_slots(lib, **over) == status
 
 
 def test_python_binding_raises_on_bad_dtype():
