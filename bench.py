@@ -57,12 +57,14 @@ PREFILL_FLOP_PER_TOKEN = 4_194_304
 PREFILL_BYTES_PER_TOKEN = 24_832
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"gdn_segment_out": "gdn_segment.hip", "gdn_segment_maps": "gdn_segment.hip",
-                  "gdn_decode_step": "gdn_decode.hip"}
+                  "gdn_decode_step": "gdn_decode.hip", "gdn_decode_multi": "gdn_decode.hip"}
 
 
-def decode_bytes(n, hqk=16, hv=32, d=128):
+def decode_bytes(n, hqk=16, hv=32, d=128, tokens=1):
+    """Algorithmic bytes of one decode call: each state read and written once, and per token q, k
+    (bf16), v, out (bf16) and g, beta (fp32)."""
     state = n * hv * d * d * 4 * 2
-    other = n * (2 * hqk * d * 2 + hv * d * 2 + hv * d * 2 + hv * 4 * 2)
+    other = n * tokens * (2 * hqk * d * 2 + hv * d * 2 + hv * d * 2 + hv * 4 * 2)
     return state + other
 
 
@@ -336,6 +338,30 @@ def main():
         result["decode"]["graph_replay"]["N8"] = graph_vs_eager(decode8, args.steps, torch)
         log(f"[bench] decode graph replay {result['decode']['graph_replay']}")
         del d8, st8, o8
+
+        # Multi-token step: 4 tokens per sequence from one state (draft verification), 256 sequences.
+        tk = 4
+        ym = I.draw(lengths=[tk] * n, hqk=y.hqk, hv=y.hv, dk=y.dk, dtype="bf16", seed=1003, s0_std=0.01,
+                    name=f"qwen3next_gdn_decode_multi_N{n}_k{tk}")
+        dm = to_device(ym, dev)
+        stm = dm["s0"].clone()
+        om = torch.empty_like(dm["v"])
+
+        def decode_multi():
+            gdn.gdn_decode_multi(dm["q"], dm["k"], dm["v"], dm["g"], dm["beta"], stm, tk, out=om)
+
+        mms, mkern = time_calls(decode_multi, args.steps, args.warmup, torch)
+        mkms = mkern.get("gdn_decode_multi", (0, mms))[1]
+        mbytes = decode_bytes(n, tokens=tk)
+        mgbs = mbytes / (mkms / 1e3) / 1e9
+        result["decode_multi"] = {"workload": ym.name, "tokens_per_seq": tk, "ms_per_step": mms,
+                                  "kernel_ms_per_launch": mkms, "bytes_per_step": mbytes,
+                                  "tokens_per_s": n * tk / (mms / 1e3),
+                                  "roofline": {"kernel": "gdn_decode_multi", "bound": "hbm", "achieved": mgbs,
+                                               "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": mgbs / PEAK_HBM_GBS,
+                                               "traffic": recorded_traffic("gdn_decode_multi", ym.name)}}
+        log(f"[bench] multi-token decode {mms:.3f} ms/step, {mgbs:.1f} GB/s")
+        del dm, stm, om
 
     if args.calibration_copy:
         a_ = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

@@ -183,6 +183,37 @@ gdn_status_t gdn_prefill_slots(const void* q, const void* k, const void* v,
                                void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Multi-token decode step: num_tokens consecutive tokens per sequence from its
+ * state in one call, as when a model's multi-token-prediction drafts are
+ * verified (page "Qwen3-Next and vLLM: Advancing Efficient Long-Context AI with
+ * Hybrid Architecture", section "Multi-Token Prediction for Acceleration").
+ * Same recurrence as gdn_decode_step applied num_tokens times; the state is
+ * read once and written once.
+ *
+ *   q, k          [num_seqs * num_tokens, num_qk_heads, d_k]   dtype; token t of
+ *                 sequence n is row n * num_tokens + t
+ *   v             [num_seqs * num_tokens, num_v_heads, d_v]    dtype
+ *   g, beta       [num_seqs * num_tokens, num_v_heads]         float
+ *   state         [num_seqs, num_v_heads, d_v, d_k] float, updated in place to
+ *                 the state after the last token; with state_indices != NULL a
+ *                 state pool [num_slots, ...] as for gdn_decode_step_slots
+ *                 (padding entries: zero outputs, no state access)
+ *   out           [num_seqs * num_tokens, num_v_heads, d_v]    dtype, written
+ *   token_states  [num_seqs * num_tokens, num_v_heads, d_v, d_k] float: the state
+ *                 after each token (so that a caller can resume from the last
+ *                 accepted draft token), or NULL
+ * 1 <= num_tokens <= 64 (GDN_ERR_INVALID_ARG below 1, GDN_ERR_UNSUPPORTED above
+ * 64: use gdn_prefill). Other checks and statuses as for gdn_decode_step.
+ */
+gdn_status_t gdn_decode_multi(const void* q, const void* k, const void* v,
+                              const float* g, const float* beta,
+                              float* state, const int32_t* state_indices, int32_t num_slots,
+                              int32_t num_seqs, int32_t num_tokens,
+                              int32_t num_qk_heads, int32_t num_v_heads,
+                              int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype,
+                              void* out, float* token_states, void* stream);
+
+/*
  * Instrumentation (for benchmarks and profiling; process-global, not
  * thread-safe, not for graph capture). After gdn_profile_start(), every kernel
  * the library launches is bracketed by a pair of HIP events recorded on the

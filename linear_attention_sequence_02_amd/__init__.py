@@ -14,7 +14,7 @@ import threading
 
 import torch
 
-__all__ = ["gdn_prefill", "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots",
+__all__ = ["gdn_prefill", "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots", "gdn_decode_multi",
            "gdn_prefill_workspace_size", "gdn_prefill_segment_chunks",
            "gdn_status_string",
            "gdn_build_info", "gdn_profile_start", "gdn_profile_stop", "GDN_BF16", "GDN_FP32", "GdnError", "library_path"]
@@ -55,6 +55,8 @@ def _load():
             lib.gdn_decode_step.argtypes = [_vp] * 6 + [_i32] * 5 + [_f32, ctypes.c_int, _vp, _vp]
             lib.gdn_decode_step_slots.restype = ctypes.c_int
             lib.gdn_decode_step_slots.argtypes = [_vp] * 7 + [_i32] * 6 + [_f32, ctypes.c_int, _vp, _vp]
+            lib.gdn_decode_multi.restype = ctypes.c_int
+            lib.gdn_decode_multi.argtypes = [_vp] * 7 + [_i32] * 7 + [_f32, ctypes.c_int, _vp, _vp, _vp]
             lib.gdn_prefill_slots.restype = ctypes.c_int
             lib.gdn_prefill_slots.argtypes = ([_vp] * 8 + [_i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                                           ctypes.c_int, _vp, _vp, _sz, _vp])
@@ -260,3 +262,40 @@ def gdn_prefill_slots(q, k, v, g, beta, state_pool, state_indices, has_initial_s
     if st != GDN_OK:
         raise GdnError(st, "gdn_prefill_slots")
     return out
+
+
+def gdn_decode_multi(q, k, v, g, beta, state, num_tokens: int, *, state_indices=None, scale: float = 1.0,
+                     out=None, token_states=None, stream=None):
+    """num_tokens consecutive tokens per sequence from its state. q, k [N * num_tokens, Hqk, d], v
+    [N * num_tokens, Hv, d] (token t of sequence n at row n * num_tokens + t), g, beta [N * num_tokens, Hv];
+    state [N, Hv, d, d] fp32 (or a pool [S, Hv, d, d] with state_indices int32 [N]) advanced in place.
+    token_states: None, True (allocate) or a [N * num_tokens, Hv, d, d] fp32 tensor for the state after
+    every token. Returns (out, token_states)."""
+    dev = q.device
+    _check(q, "q", device=dev)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, q.dtype, dev)
+    for name, t in (("g", g), ("beta", beta), ("state", state)):
+        _check(t, name, torch.float32, dev)
+    _check(state_indices, "state_indices", torch.int32, dev)
+    rows, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    if num_tokens < 1 or rows % num_tokens:
+        raise ValueError(f"{rows} token rows are not a whole number of sequences of {num_tokens} tokens")
+    N = rows // num_tokens
+    if out is None:
+        out = torch.empty((rows, hv, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", q.dtype, dev)
+    if token_states is True:
+        token_states = torch.empty((rows, hv, dv, dk), dtype=torch.float32, device=dev)
+    elif token_states is False:
+        token_states = None
+    _check(token_states, "token_states", torch.float32, dev)
+    num_slots = state.shape[0] if state_indices is not None else 0
+    st = _load().gdn_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                  _ptr(state_indices), num_slots, N, num_tokens, hqk, hv, dk, dv, float(scale), dt,
+                                  _ptr(out), _ptr(token_states), _stream(stream, dev))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_decode_multi")
+    return out, token_states

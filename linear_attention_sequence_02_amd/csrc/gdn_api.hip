@@ -77,11 +77,12 @@ gdn_status_t prefill_impl(const void* q, const void* k, const void* v, const flo
     return hip_status(a.bf16 ? gdn::launch_prefill_bf16(a, s) : gdn::launch_prefill_f32(a, s));
 }
 
-// Shared body of gdn_decode_step and gdn_decode_step_slots.
+// Shared body of gdn_decode_step, gdn_decode_step_slots and gdn_decode_multi.
 gdn_status_t decode_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
                          float* state, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads,
                          int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype, void* out, void* stream,
-                         const int32_t* state_indices, int32_t num_slots) {
+                         const int32_t* state_indices, int32_t num_slots, int32_t num_tokens = 1,
+                         float* token_states = nullptr, bool multi = false) {
     if (num_qk_heads <= 0 || num_v_heads <= 0 || d_k <= 0 || d_v <= 0 || num_seqs < 0)
         return GDN_ERR_INVALID_ARG;
     if (num_v_heads % num_qk_heads != 0) return GDN_ERR_INVALID_ARG;
@@ -91,12 +92,15 @@ gdn_status_t decode_impl(const void* q, const void* k, const void* v, const floa
     if (!q || !k || !v || !g || !beta || !out) return GDN_ERR_INVALID_ARG;
     if (!state && !(state_indices && num_slots == 0)) return GDN_ERR_INVALID_ARG;
     if ((int64_t)num_seqs * num_v_heads > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    if ((int64_t)num_seqs * num_tokens * num_v_heads > INT32_MAX) return GDN_ERR_UNSUPPORTED;
     gdn::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.out = out;
     a.state_indices = state_indices; a.num_slots = num_slots;
     a.num_seqs = num_seqs; a.num_qk_heads = num_qk_heads; a.num_v_heads = num_v_heads; a.d = d_k;
     a.scale = scale; a.bf16 = (dtype == GDN_BF16);
-    return hip_status(gdn::launch_decode(a, static_cast<hipStream_t>(stream)));
+    a.num_tokens = num_tokens; a.token_states = token_states;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(multi ? gdn::launch_decode_multi(a, s) : gdn::launch_decode(a, s));
 }
 
 }  // namespace
@@ -134,6 +138,23 @@ gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v, const 
     if (num_seqs > 0 && state == nullptr) return GDN_ERR_INVALID_ARG;
     return decode_impl(q, k, v, g, beta, state, num_seqs, num_qk_heads, num_v_heads, d_k, d_v, scale, dtype, out,
                        stream, nullptr, 0);
+}
+
+gdn_status_t gdn_decode_multi(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                              float* state, const int32_t* state_indices, int32_t num_slots, int32_t num_seqs,
+                              int32_t num_tokens, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k, int32_t d_v,
+                              float scale, gdn_dtype_t dtype, void* out, float* token_states, void* stream) {
+    if (num_tokens < 1) return GDN_ERR_INVALID_ARG;
+    if (num_tokens > 64) return GDN_ERR_UNSUPPORTED;
+    if (state_indices) {
+        if (num_slots < 0) return GDN_ERR_INVALID_ARG;
+        if (num_slots > 0 && state == nullptr) return GDN_ERR_INVALID_ARG;
+    } else {
+        if (num_seqs > 0 && state == nullptr) return GDN_ERR_INVALID_ARG;
+        num_slots = 0;
+    }
+    return decode_impl(q, k, v, g, beta, state, num_seqs, num_qk_heads, num_v_heads, d_k, d_v, scale, dtype, out,
+                       stream, state_indices, num_slots, num_tokens, token_states, true);
 }
 
 gdn_status_t gdn_decode_step_slots(const void* q, const void* k, const void* v, const float* g, const float* beta,

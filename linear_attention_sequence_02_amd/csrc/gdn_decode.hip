@@ -29,6 +29,8 @@
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
+#include <type_traits>
+
 namespace gdn {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -143,6 +145,179 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
             if constexpr (BF16) reinterpret_cast<uint16_t*>(out_)[vo_base + row] = float_to_bf16_bits(o);
             else reinterpret_cast<float*>(out_)[vo_base + row] = o;
         }
+    }
+}
+
+// Several tokens per sequence from one state (draft tokens of multi-token
+// prediction, verified in one call): the state is read once, advanced token by
+// token in registers with the same per-token update as above, and written
+// once; optionally the state after every token is stored as well, so that a
+// caller can resume from the last accepted token. Inputs are token-major per
+// sequence: token t of sequence n is row n * num_tokens + t.
+template <int D, bool BF16>
+__global__ __launch_bounds__(512) void decode_multi_kernel(
+    const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state, int32_t num_tokens,
+    int32_t num_qk_heads, int32_t num_v_heads, float scale, void* __restrict__ out_,
+    float* __restrict__ token_states, const int32_t* __restrict__ state_indices, int32_t num_slots) {
+    constexpr int L = D / 16;
+    constexpr int NT = (D * L < 512) ? D * L : 512;
+    constexpr int ROWS_PER_PASS = NT / L;
+    constexpr int R = D / ROWS_PER_PASS;
+    static_assert(R * ROWS_PER_PASS == D, "rows must tile");
+
+    const int tid = threadIdx.x;
+    const int c = tid % L;
+    const int r0 = tid / L;
+    const int64_t sh = blockIdx.x;               // sequence * num_v_heads + head
+    const int n = static_cast<int>(sh / num_v_heads);
+    const int h = static_cast<int>(sh % num_v_heads);
+    const int hq = h / (num_v_heads / num_qk_heads);
+
+    const int64_t srow = state_row(state_indices, num_slots, n);
+    if (srow < 0) {   // padding entry: zero outputs, no state access
+        if (c == 0) {
+            for (int t = 0; t < num_tokens; ++t) {
+                const int64_t ob = (((int64_t)n * num_tokens + t) * num_v_heads + h) * D;
+#pragma unroll
+                for (int m = 0; m < R; ++m) {
+                    const int row = r0 + m * ROWS_PER_PASS;
+                    if constexpr (BF16) reinterpret_cast<uint16_t*>(out_)[ob + row] = 0;
+                    else reinterpret_cast<float*>(out_)[ob + row] = 0.f;
+                }
+            }
+        }
+        return;
+    }
+    // One token's inputs for this lane: k and q slices, the value of each owned
+    // row, g and beta. Token t + 1's are requested before token t is computed.
+    using raw_t = typename std::conditional<BF16, uint2, float4>::type;
+    struct TokIn {
+        raw_t kraw[4], qraw[4];
+        float vi[R];
+        float g, b;
+    };
+    auto load_tok = [&](int t, TokIn& in) {
+        const int64_t tok = (int64_t)n * num_tokens + t;
+        const int64_t qk_base = (tok * num_qk_heads + hq) * D;
+        const raw_t* k2 = reinterpret_cast<const raw_t*>(reinterpret_cast<const char*>(k_) + qk_base * (BF16 ? 2 : 4));
+        const raw_t* q2 = reinterpret_cast<const raw_t*>(reinterpret_cast<const char*>(q_) + qk_base * (BF16 ? 2 : 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            in.kraw[i] = k2[c + L * i];
+            in.qraw[i] = q2[c + L * i];
+        }
+        const int64_t gb = tok * num_v_heads + h;
+#pragma unroll
+        for (int m = 0; m < R; ++m) {
+            const int row = r0 + m * ROWS_PER_PASS;
+            if constexpr (BF16) in.vi[m] = bf16_bits_to_float(reinterpret_cast<const uint16_t*>(v_)[gb * D + row]);
+            else in.vi[m] = reinterpret_cast<const float*>(v_)[gb * D + row];
+        }
+        in.g = g[gb];
+        in.b = beta[gb];
+    };
+
+    f32x4* S = reinterpret_cast<f32x4*>(state + (srow * num_v_heads + h) * (int64_t)D * D);
+    f32x4 s[R][4];
+#pragma unroll
+    for (int m = 0; m < R; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s[m][i] = __builtin_nontemporal_load(&S[(r0 + m * ROWS_PER_PASS) * (D / 4) + c + L * i]);
+    TokIn cur, nxt;
+    load_tok(0, cur);
+
+    for (int t = 0; t < num_tokens; ++t) {
+        if (t + 1 < num_tokens) load_tok(t + 1, nxt);
+        const int64_t gb = ((int64_t)n * num_tokens + t) * num_v_heads + h;
+        // Key / query element e of this lane's slice i (bf16: from the packed bits).
+        auto kf = [&](int i, int e) {
+            if constexpr (BF16) {
+                const uint32_t w = (e < 2) ? cur.kraw[i].x : cur.kraw[i].y;
+                return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            } else {
+                return e == 0 ? cur.kraw[i].x : e == 1 ? cur.kraw[i].y : e == 2 ? cur.kraw[i].z : cur.kraw[i].w;
+            }
+        };
+        auto qf = [&](int i, int e) {
+            if constexpr (BF16) {
+                const uint32_t w = (e < 2) ? cur.qraw[i].x : cur.qraw[i].y;
+                return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            } else {
+                return e == 0 ? cur.qraw[i].x : e == 1 ? cur.qraw[i].y : e == 2 ? cur.qraw[i].z : cur.qraw[i].w;
+            }
+        };
+        const float alpha = exp_nonpos(cur.g);
+        float kq = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kq = fmaf(kf(i, e), qf(i, e), kq);
+        kq = group_sum<L>(kq);
+        const int64_t vo_base = gb * D;
+#pragma unroll
+        for (int m = 0; m < R; ++m) {
+            const int row = r0 + m * ROWS_PER_PASS;
+            float a = 0.f, bq = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a = fmaf(s[m][i][e], kf(i, e), a);
+                    bq = fmaf(s[m][i][e], qf(i, e), bq);
+                }
+            a = group_sum<L>(a);
+            bq = group_sum<L>(bq);
+            const float u = cur.b * (cur.vi[m] - alpha * a);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[m][i][e] = fmaf(alpha, s[m][i][e], u * kf(i, e));
+            if (c == 0) {
+                const float o = scale * fmaf(alpha, bq, u * kq);
+                if constexpr (BF16) reinterpret_cast<uint16_t*>(out_)[vo_base + row] = float_to_bf16_bits(o);
+                else reinterpret_cast<float*>(out_)[vo_base + row] = o;
+            }
+        }
+        if (token_states) {
+            f32x4* TS = reinterpret_cast<f32x4*>(token_states + gb * (int64_t)D * D);
+#pragma unroll
+            for (int m = 0; m < R; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    __builtin_nontemporal_store(s[m][i], &TS[(r0 + m * ROWS_PER_PASS) * (D / 4) + c + L * i]);
+        }
+        cur = nxt;
+    }
+#pragma unroll
+    for (int m = 0; m < R; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_nontemporal_store(s[m][i], &S[(r0 + m * ROWS_PER_PASS) * (D / 4) + c + L * i]);
+}
+
+template <int D, bool BF16>
+static hipError_t launch_decode_multi_t(const DecodeArgs& a, hipStream_t stream) {
+    constexpr int L = D / 16;
+    constexpr int NT = (D * L < 512) ? D * L : 512;
+    const int64_t blocks = (int64_t)a.num_seqs * a.num_v_heads;
+    prof::begin(stream, "gdn_decode_multi");
+    hipLaunchKernelGGL((decode_multi_kernel<D, BF16>), dim3((unsigned)blocks), dim3(NT), 0, stream,
+                       a.q, a.k, a.v, a.g, a.beta, a.state, a.num_tokens, a.num_qk_heads, a.num_v_heads, a.scale,
+                       a.out, a.token_states, a.state_indices, a.num_slots);
+    prof::end(stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t stream) {
+    const bool bf = a.bf16;
+    switch (a.d) {
+        case 16: return bf ? launch_decode_multi_t<16, true>(a, stream) : launch_decode_multi_t<16, false>(a, stream);
+        case 32: return bf ? launch_decode_multi_t<32, true>(a, stream) : launch_decode_multi_t<32, false>(a, stream);
+        case 64: return bf ? launch_decode_multi_t<64, true>(a, stream) : launch_decode_multi_t<64, false>(a, stream);
+        case 128: return bf ? launch_decode_multi_t<128, true>(a, stream) : launch_decode_multi_t<128, false>(a, stream);
+        default: return hipErrorInvalidValue;
     }
 }
 

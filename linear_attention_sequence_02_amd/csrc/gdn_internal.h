@@ -19,6 +19,8 @@ struct DecodeArgs {
     void* out;
     const int32_t* state_indices;   // null: sequence n uses state row n; else row state_indices[n]
     int32_t num_slots;              // rows in the state pool (with state_indices)
+    int32_t num_tokens = 1;         // tokens per sequence (multi-token step)
+    float* token_states = nullptr;  // multi-token step: state after every token, or null
     int32_t num_seqs, num_qk_heads, num_v_heads, d;
     float scale;
     bool bf16;
@@ -61,6 +63,7 @@ void end(hipStream_t s);
 }  // namespace prof
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 int cp_segment_chunks(int64_t total_tokens, int32_t num_seqs, int32_t num_v_heads);

@@ -31,6 +31,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert set(declared_functions()) == {"gdn_prefill_workspace_size", "gdn_prefill_segment_chunks", "gdn_prefill",
                                          "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots",
+                                         "gdn_decode_multi",
                                          "gdn_status_string", "gdn_build_info", "gdn_profile_start",
                                          "gdn_profile_stop"}
 
@@ -153,6 +154,33 @@ def test_decode_slots_rejects(lib, over, status):
 
 def test_decode_slots_with_no_sequences_is_a_no_op(lib):
     assert _decode_slots(lib, n=0, idx=None) == gdn.GDN_OK
+
+
+def _decode_multi(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, idx=None, slots=0, n=4, tk=3, hqk=16, hv=32,
+             dk=128, dv=128, scale=1.0, dt=gdn.GDN_BF16, out=FAKE, ts=None, stream=None)
+    a.update(over)
+    return lib.gdn_decode_multi(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"], a["idx"], a["slots"],
+                                a["n"], a["tk"], a["hqk"], a["hv"], a["dk"], a["dv"], a["scale"], a["dt"], a["out"],
+                                a["ts"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(tk=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(tk=65), gdn.GDN_ERR_UNSUPPORTED),                 # long runs belong to the chunked prefill
+    (dict(state=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(idx=FAKE, slots=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(idx=FAKE, slots=4, state=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(hqk=5), gdn.GDN_ERR_INVALID_ARG),
+    (dict(out=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dk=100, dv=100), gdn.GDN_ERR_UNSUPPORTED),
+])
+def test_decode_multi_rejects(lib, over, status):
+    assert _decode_multi(lib, **over) == status
+
+
+def test_decode_multi_with_no_sequences_is_a_no_op(lib):
+    assert _decode_multi(lib, n=0) == gdn.GDN_OK
 
 
 def _prefill_slots(lib, **over):
