@@ -14,7 +14,15 @@ Where the pages are silent (they state the rule in words only), the readings
 are: decay before the delta correction; read-out after the write; state
 element [i][j] = (value index, key index); V head h uses QK head
 h // (Hv // Hqk); the query scale is an argument (1.0 unless a test says
-otherwise); q and k arrive L2-normalised.
+otherwise); q and k arrive L2-normalised, or, with qk_l2norm=True (the
+library's in-kernel normalisation mode, an input prologue that page
+"Qwen3-Next-80B-A3B-Instruct", section "Quickstart", points to with the
+flash-linear-attention kernels), are normalised here first, per token and
+head, as x / sqrt(sum(x^2) + 1e-6) in fp64 (the epsilon is this library's
+reading; the pages give none).
+
+  upcast(x)       exact fp64 value of a bf16-bit / fp32 / fp64 array.
+  qk_normalize(x) that normalisation along the last axis, fp64.
 """
 from __future__ import annotations
 
@@ -64,16 +72,37 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
+QK_L2NORM_EPS = 1e-6
+
+
+def upcast(x) -> np.ndarray:
+    """Exact fp64 values of an input array: bf16 bit patterns (uint16), float32 or float64."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def qk_normalize(x, eps: float = QK_L2NORM_EPS) -> np.ndarray:
+    """Each vector along the last axis divided by sqrt(its squared length + eps), in fp64."""
+    x = upcast(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
 def recurrent(q, k, v, g, beta, s0=None, cu_seqlens=None, *, scale: float = 1.0,
-              heads=None, threads: int = 0, mutant: int = 0, return_threads: bool = False):
+              heads=None, threads: int = 0, mutant: int = 0, return_threads: bool = False,
+              qk_l2norm: bool = False):
     """Run the fp64 recurrence.
 
     q, k: [T, Hqk, dk]; v: [T, Hv, dv] as uint16 (bf16 bits), float32 or float64.
     g, beta: [T, Hv]; s0: [N, Hv, dv, dk] or None (zeros); all float32 or float64.
     cu_seqlens: [N + 1] offsets (None: one sequence of length T).
     heads: (h_begin, h_end) to compute only those V heads (default all).
+    qk_l2norm: normalise q and k first (qk_normalize); the run is then in fp64 throughout.
     Returns (out [T, nh, dv], final_state [N, nh, dv, dk]) in float64.
     """
+    if qk_l2norm:
+        q, k, v = qk_normalize(q), qk_normalize(k), upcast(v)
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
     v = np.ascontiguousarray(v)

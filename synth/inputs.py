@@ -17,7 +17,9 @@ Conventions shared with the library's C header:
 
 q and k are L2-normalised per token per head in fp64 before the cast to the
 storage dtype: the normalisation is a precondition of the layer, done by its
-caller, so neither side renormalises.
+caller, so neither side renormalises. For the library's in-kernel
+normalisation mode, draw(qk_unit=False) returns q and k rows of varied length
+instead (N(0, 1) times 10^U(-1, 1) per row).
 """
 from __future__ import annotations
 
@@ -92,6 +94,16 @@ def _unit_rows(seed: int, stream: int, shape) -> np.ndarray:
     return _fill_blocks(shape, fn)
 
 
+def _scaled_rows(seed: int, stream: int, shape) -> np.ndarray:
+    """N(0,1) vectors along the last axis times 10^U(-1, 1) per vector (lengths spread over two
+    decades); the factors come from their own child generators (stream + 10)."""
+    def fn(b, shp):
+        x = _block_rng(seed, stream, b).standard_normal(shp, dtype=np.float32).astype(np.float64)
+        f = 10.0 ** _block_rng(seed, stream + 10, b).uniform(-1.0, 1.0, size=shp[:-1] + (1,))
+        return x * f
+    return _fill_blocks(shape, fn)
+
+
 def _normal_rows(seed: int, stream: int, shape) -> np.ndarray:
     return _fill_blocks(shape, lambda b, shp: _block_rng(seed, stream, b).standard_normal(shp, dtype=np.float32))
 
@@ -153,6 +165,7 @@ def draw(
     varlen_draw=None,
     fixed_g: float | None = None,
     fixed_beta: float | None = None,
+    qk_unit: bool = True,
 ) -> GdnInputs:
     """Draw one seeded input set.
 
@@ -163,7 +176,8 @@ def draw(
     g = -softplus(N(g_mean, 1)), beta = sigmoid(N(0, 1)), v ~ N(0, 1),
     initial states s0_std * N(0, 1) when s0_std is given (else none).
     fixed_g / fixed_beta replace the drawn values by a constant (used by
-    the special cases whose closed forms the tests check).
+    the special cases whose closed forms the tests check). qk_unit=False
+    leaves q and k unnormalised (for the in-kernel normalisation mode).
     """
     if dtype not in ("bf16", "fp32"):
         raise ValueError(dtype)
@@ -180,8 +194,9 @@ def draw(
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
 
-    q = _unit_rows(seed, 1, (T, hqk, dk))
-    k = _unit_rows(seed, 2, (T, hqk, dk))
+    rows = _unit_rows if qk_unit else _scaled_rows
+    q = rows(seed, 1, (T, hqk, dk))
+    k = rows(seed, 2, (T, hqk, dk))
     v = _normal_rows(seed, 3, (T, hv, dv))
     g = (-_softplus(rng.standard_normal((T, hv)) + g_mean)).astype(np.float32)
     beta = _sigmoid(rng.standard_normal((T, hv))).astype(np.float32)
