@@ -21,6 +21,11 @@ Roofline figures use algorithmic work only:
       plus q, k, v, g, beta, out); also on a state pool addressed by slot
       ("decode.slots"), and as eager calls against graph replays, wall clock
       per step ("decode.graph_replay", 256 and 8 sequences; a graph holds 16 steps)
+  multi-token decode ("decode_multi"): 4 tokens per sequence from one state,
+      256 sequences: the state read and written once plus 4 tokens' inputs and
+      outputs, 1,099,169,792 bytes per step
+  with q and k L2-normalised in the kernels ("prefill_qk_l2norm",
+      "decode.qk_l2norm"): the same inputs and algorithmic work
 Peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8.0 TB/s.
 "step_ms" gives the mean, median and min of the prefill step (a further pass
 with events around each call). The timed run behind `value` has no
@@ -280,6 +285,20 @@ def main():
     }
     out_host = out.view(torch.int16).cpu().numpy()
     fin_host = fin.cpu().numpy()
+
+    # The same step with q and k L2-normalised in the kernels (GDN_FLAG_QK_L2NORM), on the same inputs.
+    out_n, fin_n = torch.empty_like(out), torch.empty_like(fin)
+
+    def prefill_norm():
+        gdn.gdn_prefill_ex(d["q"], d["k"], d["v"], d["g"], d["beta"], None, fin_n, None, None, None,
+                           flags=gdn.GDN_FLAG_QK_L2NORM, out=out_n, workspace=ws)
+
+    nms, nkern = time_calls(prefill_norm, args.steps, args.warmup, torch)
+    result["prefill_qk_l2norm"] = {"ms_per_step": nms, "tokens_per_s": x.T / (nms / 1e3),
+                                   "relative_to_plain": nms / ms,
+                                   "kernels_ms_per_launch": {k_: v_[1] for k_, v_ in nkern.items()}}
+    log(f"[bench] prefill with in-kernel q/k normalisation {nms:.3f} ms/step")
+    del out_n, fin_n
     del d, out, fin, ws
     torch.cuda.empty_cache()
 
@@ -318,6 +337,18 @@ def main():
 
         sms, skern = time_calls(decode_slots, args.steps, args.warmup, torch)
         skms = skern.get("gdn_decode_step", (0, sms))[1]
+        st_n = dd["s0"].clone()
+
+        def decode_norm():
+            gdn.gdn_decode_ex(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], st_n, flags=gdn.GDN_FLAG_QK_L2NORM,
+                              out=dout)
+
+        qms, qkern = time_calls(decode_norm, args.steps, args.warmup, torch)
+        qkms = qkern.get("gdn_decode_step", (0, qms))[1]
+        result["decode"]["qk_l2norm"] = {"ms_per_step": qms, "kernel_ms_per_launch": qkms,
+                                         "GB_per_s": nbytes / (qkms / 1e3) / 1e9,
+                                         "frac_hbm_peak": nbytes / (qkms / 1e3) / 1e9 / PEAK_HBM_GBS}
+        del st_n
         result["decode"]["slots"] = {"pool_slots": slots, "ms_per_step": sms, "kernel_ms_per_launch": skms,
                                      "GB_per_s": nbytes / (skms / 1e3) / 1e9,
                                      "frac_hbm_peak": nbytes / (skms / 1e3) / 1e9 / PEAK_HBM_GBS}

@@ -214,6 +214,54 @@ gdn_status_t gdn_decode_multi(const void* q, const void* k, const void* v,
                               void* out, float* token_states, void* stream);
 
 /*
+ * General forms with option flags. Every entry point above is one of these
+ * with flags = 0.
+ *
+ * Flags (bitwise OR):
+ *   GDN_FLAG_QK_L2NORM  the kernels L2-normalise each token's q and k per QK
+ *                       head before using them, x / sqrt(sum(x^2) + 1e-6) in
+ *                       fp32 (bf16 inputs: the staged keys and queries are the
+ *                       normalised values rounded to bf16). It lifts the
+ *                       unit-length precondition on q and k: the input
+ *                       prologue that page "Qwen3-Next-80B-A3B-Instruct",
+ *                       section "Quickstart", leaves to the flash-linear-
+ *                       attention kernels. (The epsilon is this library's
+ *                       choice; the pages give none.)
+ * Unknown flag bits are GDN_ERR_INVALID_ARG.
+ */
+#define GDN_FLAG_QK_L2NORM 1u
+
+/*
+ * gdn_prefill_ex: with state_indices == NULL, initial_state and final_state
+ * are [num_seqs, ...] arrays as in gdn_prefill (has_initial_state and
+ * num_slots are ignored); otherwise both are pools of num_slots rows
+ * addressed as in gdn_prefill_slots (they may be the same pool), where a NULL
+ * initial_state means zeros and a NULL final_state writes nothing.
+ */
+gdn_status_t gdn_prefill_ex(const void* q, const void* k, const void* v,
+                            const float* g, const float* beta,
+                            const float* initial_state, float* final_state,
+                            const int32_t* state_indices, const int32_t* has_initial_state,
+                            int32_t num_slots,
+                            const int32_t* cu_seqlens, int32_t num_seqs,
+                            int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads,
+                            int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype, uint32_t flags,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_decode_ex: gdn_decode_multi with flags (num_tokens = 1 and
+ * token_states = NULL is gdn_decode_step, or gdn_decode_step_slots with
+ * state_indices).
+ */
+gdn_status_t gdn_decode_ex(const void* q, const void* k, const void* v,
+                           const float* g, const float* beta,
+                           float* state, const int32_t* state_indices, int32_t num_slots,
+                           int32_t num_seqs, int32_t num_tokens,
+                           int32_t num_qk_heads, int32_t num_v_heads,
+                           int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype, uint32_t flags,
+                           void* out, float* token_states, void* stream);
+
+/*
  * Instrumentation (for benchmarks and profiling; process-global, not
  * thread-safe, not for graph capture). After gdn_profile_start(), every kernel
  * the library launches is bracketed by a pair of HIP events recorded on the

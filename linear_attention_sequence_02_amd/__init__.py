@@ -15,12 +15,14 @@ import threading
 import torch
 
 __all__ = ["gdn_prefill", "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots", "gdn_decode_multi",
+           "gdn_prefill_ex", "gdn_decode_ex", "GDN_FLAG_QK_L2NORM",
            "gdn_prefill_workspace_size", "gdn_prefill_segment_chunks",
            "gdn_status_string",
            "gdn_build_info", "gdn_profile_start", "gdn_profile_stop", "GDN_BF16", "GDN_FP32", "GdnError", "library_path"]
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(5)
 GDN_BF16, GDN_FP32 = 0, 1
+GDN_FLAG_QK_L2NORM = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libgdn.so")
@@ -57,6 +59,12 @@ def _load():
             lib.gdn_decode_step_slots.argtypes = [_vp] * 7 + [_i32] * 6 + [_f32, ctypes.c_int, _vp, _vp]
             lib.gdn_decode_multi.restype = ctypes.c_int
             lib.gdn_decode_multi.argtypes = [_vp] * 7 + [_i32] * 7 + [_f32, ctypes.c_int, _vp, _vp, _vp]
+            lib.gdn_prefill_ex.restype = ctypes.c_int
+            lib.gdn_prefill_ex.argtypes = ([_vp] * 9 + [_i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
+                                                       ctypes.c_int, ctypes.c_uint32, _vp, _vp, _sz, _vp])
+            lib.gdn_decode_ex.restype = ctypes.c_int
+            lib.gdn_decode_ex.argtypes = ([_vp] * 7 + [_i32] * 7 + [_f32, ctypes.c_int, ctypes.c_uint32]
+                                          + [_vp, _vp, _vp])
             lib.gdn_prefill_slots.restype = ctypes.c_int
             lib.gdn_prefill_slots.argtypes = ([_vp] * 8 + [_i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                                           ctypes.c_int, _vp, _vp, _sz, _vp])
@@ -298,4 +306,76 @@ def gdn_decode_multi(q, k, v, g, beta, state, num_tokens: int, *, state_indices=
                                   _ptr(out), _ptr(token_states), _stream(stream, dev))
     if st != GDN_OK:
         raise GdnError(st, "gdn_decode_multi")
+    return out, token_states
+
+
+def gdn_prefill_ex(q, k, v, g, beta, initial_state=None, final_state=None, state_indices=None,
+                   has_initial_state=None, cu_seqlens=None, *, flags: int = 0, scale: float = 1.0, out=None,
+                   workspace=None, stream=None):
+    """General prefill with option flags (GDN_FLAG_QK_L2NORM: q and k normalised in the kernels).
+    Without state_indices, initial_state / final_state are [N, Hv, d, d] arrays (or None); with it they
+    are pools [S, Hv, d, d] addressed by slot. Returns out."""
+    dev = q.device
+    _check(q, "q", device=dev)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, q.dtype, dev)
+    for name, t in (("g", g), ("beta", beta), ("initial_state", initial_state), ("final_state", final_state)):
+        _check(t, name, torch.float32, dev)
+    for name, t in (("state_indices", state_indices), ("has_initial_state", has_initial_state),
+                    ("cu_seqlens", cu_seqlens)):
+        _check(t, name, torch.int32, dev)
+    T, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    n = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    num_slots = 0
+    if state_indices is not None:
+        pool = initial_state if initial_state is not None else final_state
+        num_slots = 0 if pool is None else pool.shape[0]
+    if out is None:
+        out = torch.empty((T, hv, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", q.dtype, dev)
+    need = gdn_prefill_workspace_size(T, n, hqk, hv, dk, dv, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _load().gdn_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                _ptr(final_state), _ptr(state_indices), _ptr(has_initial_state), num_slots,
+                                _ptr(cu_seqlens), n, T, hqk, hv, dk, dv, float(scale), dt, int(flags), _ptr(out),
+                                _ptr(workspace), ws_bytes, _stream(stream, dev))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_prefill_ex")
+    return out
+
+
+def gdn_decode_ex(q, k, v, g, beta, state, *, num_tokens: int = 1, state_indices=None, flags: int = 0,
+                  scale: float = 1.0, out=None, token_states=None, stream=None):
+    """General decode with option flags: num_tokens tokens per sequence (layout as gdn_decode_multi),
+    optional state pool (state_indices) and per-token states. Returns (out, token_states)."""
+    dev = q.device
+    _check(q, "q", device=dev)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v)):
+        _check(t, name, q.dtype, dev)
+    for name, t in (("g", g), ("beta", beta), ("state", state)):
+        _check(t, name, torch.float32, dev)
+    _check(state_indices, "state_indices", torch.int32, dev)
+    rows, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    if num_tokens < 1 or rows % num_tokens:
+        raise ValueError(f"{rows} token rows are not a whole number of sequences of {num_tokens} tokens")
+    if out is None:
+        out = torch.empty((rows, hv, dv), dtype=q.dtype, device=dev)
+    _check(out, "out", q.dtype, dev)
+    if token_states is True:
+        token_states = torch.empty((rows, hv, dv, dk), dtype=torch.float32, device=dev)
+    elif token_states is False:
+        token_states = None
+    _check(token_states, "token_states", torch.float32, dev)
+    num_slots = state.shape[0] if state_indices is not None else 0
+    st = _load().gdn_decode_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(state_indices),
+                               num_slots, rows // num_tokens, num_tokens, hqk, hv, dk, dv, float(scale), dt,
+                               int(flags), _ptr(out), _ptr(token_states), _stream(stream, dev))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_decode_ex")
     return out, token_states

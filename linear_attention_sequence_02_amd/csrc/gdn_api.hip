@@ -23,6 +23,8 @@ gdn_status_t check_heads(int32_t hqk, int32_t hv, int32_t dk, int32_t dv, gdn_dt
 
 gdn_status_t hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
+constexpr uint32_t kKnownFlags = GDN_FLAG_QK_L2NORM;
+
 }  // namespace
 
 extern "C" {
@@ -53,9 +55,11 @@ gdn_status_t prefill_impl(const void* q, const void* k, const void* v, const flo
                           int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k,
                           int32_t d_v, float scale, gdn_dtype_t dtype, void* out, float* final_state,
                           void* workspace, size_t workspace_bytes, void* stream,
-                          const int32_t* state_indices, const int32_t* has_initial, int32_t num_slots) {
+                          const int32_t* state_indices, const int32_t* has_initial, int32_t num_slots,
+                          uint32_t flags = 0) {
     gdn_status_t st = check_heads(num_qk_heads, num_v_heads, d_k, d_v, dtype);
     if (st != GDN_OK) return st;
+    if (flags & ~kKnownFlags) return GDN_ERR_INVALID_ARG;
     if (total_tokens < 0 || num_seqs < 0) return GDN_ERR_INVALID_ARG;
     if (total_tokens > INT32_MAX) return GDN_ERR_UNSUPPORTED;   // cu_seqlens are int32
     if (cu_seqlens == nullptr && num_seqs != 1) return GDN_ERR_INVALID_ARG;
@@ -73,6 +77,7 @@ gdn_status_t prefill_impl(const void* q, const void* k, const void* v, const flo
     a.out = out; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.total_tokens = total_tokens; a.num_seqs = num_seqs; a.num_qk_heads = num_qk_heads;
     a.num_v_heads = num_v_heads; a.d = d_k; a.scale = scale; a.bf16 = (dtype == GDN_BF16);
+    a.qk_norm = (flags & GDN_FLAG_QK_L2NORM) != 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return hip_status(a.bf16 ? gdn::launch_prefill_bf16(a, s) : gdn::launch_prefill_f32(a, s));
 }
@@ -82,9 +87,10 @@ gdn_status_t decode_impl(const void* q, const void* k, const void* v, const floa
                          float* state, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads,
                          int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype, void* out, void* stream,
                          const int32_t* state_indices, int32_t num_slots, int32_t num_tokens = 1,
-                         float* token_states = nullptr, bool multi = false) {
+                         float* token_states = nullptr, bool multi = false, uint32_t flags = 0) {
     if (num_qk_heads <= 0 || num_v_heads <= 0 || d_k <= 0 || d_v <= 0 || num_seqs < 0)
         return GDN_ERR_INVALID_ARG;
+    if (flags & ~kKnownFlags) return GDN_ERR_INVALID_ARG;
     if (num_v_heads % num_qk_heads != 0) return GDN_ERR_INVALID_ARG;
     if (dtype != GDN_BF16 && dtype != GDN_FP32) return GDN_ERR_INVALID_ARG;
     if (d_k != d_v || !fp32_head_size_ok(d_k)) return GDN_ERR_UNSUPPORTED;
@@ -99,8 +105,29 @@ gdn_status_t decode_impl(const void* q, const void* k, const void* v, const floa
     a.num_seqs = num_seqs; a.num_qk_heads = num_qk_heads; a.num_v_heads = num_v_heads; a.d = d_k;
     a.scale = scale; a.bf16 = (dtype == GDN_BF16);
     a.num_tokens = num_tokens; a.token_states = token_states;
+    a.qk_norm = (flags & GDN_FLAG_QK_L2NORM) != 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return hip_status(multi ? gdn::launch_decode_multi(a, s) : gdn::launch_decode(a, s));
+}
+
+// Shared body of gdn_decode_ex and gdn_decode_multi: token count, state and pool checks, then the
+// multi-token kernel (multi) or the single-step one.
+gdn_status_t decode_ex_impl(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                            float* state, const int32_t* state_indices, int32_t num_slots, int32_t num_seqs,
+                            int32_t num_tokens, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k, int32_t d_v,
+                            float scale, gdn_dtype_t dtype, uint32_t flags, void* out, float* token_states,
+                            void* stream, bool multi) {
+    if (num_tokens < 1) return GDN_ERR_INVALID_ARG;
+    if (num_tokens > 64) return GDN_ERR_UNSUPPORTED;
+    if (state_indices) {
+        if (num_slots < 0) return GDN_ERR_INVALID_ARG;
+        if (num_slots > 0 && state == nullptr) return GDN_ERR_INVALID_ARG;
+    } else {
+        if (num_seqs > 0 && state == nullptr) return GDN_ERR_INVALID_ARG;
+        num_slots = 0;
+    }
+    return decode_impl(q, k, v, g, beta, state, num_seqs, num_qk_heads, num_v_heads, d_k, d_v, scale, dtype, out,
+                       stream, state_indices, num_slots, num_tokens, token_states, multi, flags);
 }
 
 }  // namespace
@@ -140,21 +167,39 @@ gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v, const 
                        stream, nullptr, 0);
 }
 
+gdn_status_t gdn_decode_ex(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           float* state, const int32_t* state_indices, int32_t num_slots, int32_t num_seqs,
+                           int32_t num_tokens, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k, int32_t d_v,
+                           float scale, gdn_dtype_t dtype, uint32_t flags, void* out, float* token_states,
+                           void* stream) {
+    return decode_ex_impl(q, k, v, g, beta, state, state_indices, num_slots, num_seqs, num_tokens, num_qk_heads,
+                          num_v_heads, d_k, d_v, scale, dtype, flags, out, token_states, stream,
+                          num_tokens > 1 || token_states != nullptr);
+}
+
 gdn_status_t gdn_decode_multi(const void* q, const void* k, const void* v, const float* g, const float* beta,
                               float* state, const int32_t* state_indices, int32_t num_slots, int32_t num_seqs,
                               int32_t num_tokens, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k, int32_t d_v,
                               float scale, gdn_dtype_t dtype, void* out, float* token_states, void* stream) {
-    if (num_tokens < 1) return GDN_ERR_INVALID_ARG;
-    if (num_tokens > 64) return GDN_ERR_UNSUPPORTED;
+    return decode_ex_impl(q, k, v, g, beta, state, state_indices, num_slots, num_seqs, num_tokens, num_qk_heads,
+                          num_v_heads, d_k, d_v, scale, dtype, 0, out, token_states, stream, true);
+}
+
+gdn_status_t gdn_prefill_ex(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                            const float* initial_state, float* final_state, const int32_t* state_indices,
+                            const int32_t* has_initial_state, int32_t num_slots, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads,
+                            int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype, uint32_t flags, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
     if (state_indices) {
         if (num_slots < 0) return GDN_ERR_INVALID_ARG;
-        if (num_slots > 0 && state == nullptr) return GDN_ERR_INVALID_ARG;
     } else {
-        if (num_seqs > 0 && state == nullptr) return GDN_ERR_INVALID_ARG;
+        has_initial_state = nullptr;   // plain arrays: every sequence reads initial_state (if given)
         num_slots = 0;
     }
-    return decode_impl(q, k, v, g, beta, state, num_seqs, num_qk_heads, num_v_heads, d_k, d_v, scale, dtype, out,
-                       stream, state_indices, num_slots, num_tokens, token_states, true);
+    return prefill_impl(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, num_qk_heads,
+                        num_v_heads, d_k, d_v, scale, dtype, out, final_state, workspace, workspace_bytes, stream,
+                        state_indices, has_initial_state, num_slots, flags);
 }
 
 gdn_status_t gdn_decode_step_slots(const void* q, const void* k, const void* v, const float* g, const float* beta,

@@ -32,16 +32,23 @@ __device__ __forceinline__ float dpp_quad_xor1(float x) {
 __device__ __forceinline__ float dpp_quad_xor2(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
 }
+// Mirror inside the row of 16 (lane i <-> 15 - i): after the 8-lane sums it
+// pairs each lane with one of the other half row.
+__device__ __forceinline__ float dpp_row_mirror(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float dpp_half_mirror(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
 }
 
 template <int L>
 __device__ __forceinline__ float group_sum(float x) {
-    static_assert(L == 1 || L == 2 || L == 4 || L == 8, "group of 1, 2, 4 or 8 lanes");
+    static_assert(L == 1 || L == 2 || L == 4 || L == 8 || L == 16, "group of 1, 2, 4, 8 or 16 lanes");
     if constexpr (L >= 2) x += dpp_quad_xor1(x);
     if constexpr (L >= 4) x += dpp_quad_xor2(x);
     if constexpr (L >= 8) x += dpp_half_mirror(x);
+    if constexpr (L >= 16) x += dpp_row_mirror(x);
     return x;
 }
 

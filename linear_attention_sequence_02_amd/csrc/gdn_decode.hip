@@ -40,7 +40,7 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
     const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
     int32_t num_qk_heads, int32_t num_v_heads, float scale, void* __restrict__ out_,
-    const int32_t* __restrict__ state_indices, int32_t num_slots) {
+    const int32_t* __restrict__ state_indices, int32_t num_slots, int32_t qk_norm) {
     constexpr int L = D / 16;                    // lanes per state row (16 floats each)
     constexpr int NT = (D * L < 512) ? D * L : 512;
     constexpr int ROWS_PER_PASS = NT / L;
@@ -108,12 +108,27 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
     const float alpha = exp_nonpos(g[sh]);
     const float b = beta[sh];
 
+    // In-kernel L2 normalisation: k and q enter through the factors rk, rq
+    // (1 when off: every product below is then exactly the plain one).
+    float rk = 1.f, rq = 1.f;
+    if (qk_norm) {
+        float nk = 0.f, nq = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                nk = fmaf(kr[i][e], kr[i][e], nk);
+                nq = fmaf(qr[i][e], qr[i][e], nq);
+            }
+        rk = rsqrtf(group_sum<L>(nk) + kQkNormEps);
+        rq = rsqrtf(group_sum<L>(nq) + kQkNormEps);
+    }
     float kq = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) kq = fmaf(kr[i][e], qr[i][e], kq);
-    kq = group_sum<L>(kq);
+    kq = group_sum<L>(kq) * (rk * rq);
 
 #pragma unroll
     for (int m = 0; m < R; ++m) {
@@ -127,17 +142,18 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
                 bq = fmaf(s[m][i][e], qr[i][e], bq);
             }
         }
-        a = group_sum<L>(a);
-        bq = group_sum<L>(bq);
+        a = group_sum<L>(a) * rk;
+        bq = group_sum<L>(bq) * rq;
         float vi;
         if constexpr (BF16) vi = bf16_bits_to_float(reinterpret_cast<const uint16_t*>(v_)[vo_base + row]);
         else vi = reinterpret_cast<const float*>(v_)[vo_base + row];
         const float u = b * (vi - alpha * a);
+        const float uk = u * rk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             f32x4 t;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) t[e] = fmaf(alpha, s[m][i][e], u * kr[i][e]);
+            for (int e = 0; e < 4; ++e) t[e] = fmaf(alpha, s[m][i][e], uk * kr[i][e]);
             __builtin_nontemporal_store(t, &S[row * (D / 4) + c + L * i]);
         }
         if (c == 0) {
@@ -159,7 +175,8 @@ __global__ __launch_bounds__(512) void decode_multi_kernel(
     const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state, int32_t num_tokens,
     int32_t num_qk_heads, int32_t num_v_heads, float scale, void* __restrict__ out_,
-    float* __restrict__ token_states, const int32_t* __restrict__ state_indices, int32_t num_slots) {
+    float* __restrict__ token_states, const int32_t* __restrict__ state_indices, int32_t num_slots,
+    int32_t qk_norm) {
     constexpr int L = D / 16;
     constexpr int NT = (D * L < 512) ? D * L : 512;
     constexpr int ROWS_PER_PASS = NT / L;
@@ -249,12 +266,25 @@ __global__ __launch_bounds__(512) void decode_multi_kernel(
             }
         };
         const float alpha = exp_nonpos(cur.g);
+        float rk = 1.f, rq = 1.f;   // in-kernel L2 normalisation factors (1 when off)
+        if (qk_norm) {
+            float nk = 0.f, nq = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    nk = fmaf(kf(i, e), kf(i, e), nk);
+                    nq = fmaf(qf(i, e), qf(i, e), nq);
+                }
+            rk = rsqrtf(group_sum<L>(nk) + kQkNormEps);
+            rq = rsqrtf(group_sum<L>(nq) + kQkNormEps);
+        }
         float kq = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) kq = fmaf(kf(i, e), qf(i, e), kq);
-        kq = group_sum<L>(kq);
+        kq = group_sum<L>(kq) * (rk * rq);
         const int64_t vo_base = gb * D;
 #pragma unroll
         for (int m = 0; m < R; ++m) {
@@ -267,13 +297,14 @@ __global__ __launch_bounds__(512) void decode_multi_kernel(
                     a = fmaf(s[m][i][e], kf(i, e), a);
                     bq = fmaf(s[m][i][e], qf(i, e), bq);
                 }
-            a = group_sum<L>(a);
-            bq = group_sum<L>(bq);
+            a = group_sum<L>(a) * rk;
+            bq = group_sum<L>(bq) * rq;
             const float u = cur.b * (cur.vi[m] - alpha * a);
+            const float uk = u * rk;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) s[m][i][e] = fmaf(alpha, s[m][i][e], u * kf(i, e));
+                for (int e = 0; e < 4; ++e) s[m][i][e] = fmaf(alpha, s[m][i][e], uk * kf(i, e));
             if (c == 0) {
                 const float o = scale * fmaf(alpha, bq, u * kq);
                 if constexpr (BF16) reinterpret_cast<uint16_t*>(out_)[vo_base + row] = float_to_bf16_bits(o);
@@ -305,7 +336,7 @@ static hipError_t launch_decode_multi_t(const DecodeArgs& a, hipStream_t stream)
     prof::begin(stream, "gdn_decode_multi");
     hipLaunchKernelGGL((decode_multi_kernel<D, BF16>), dim3((unsigned)blocks), dim3(NT), 0, stream,
                        a.q, a.k, a.v, a.g, a.beta, a.state, a.num_tokens, a.num_qk_heads, a.num_v_heads, a.scale,
-                       a.out, a.token_states, a.state_indices, a.num_slots);
+                       a.out, a.token_states, a.state_indices, a.num_slots, a.qk_norm ? 1 : 0);
     prof::end(stream);
     return hipGetLastError();
 }
@@ -329,7 +360,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     prof::begin(stream, "gdn_decode_step");
     hipLaunchKernelGGL((decode_step_kernel<D, BF16>), dim3((unsigned)blocks), dim3(NT), 0, stream,
                        a.q, a.k, a.v, a.g, a.beta, a.state, a.num_qk_heads, a.num_v_heads, a.scale, a.out,
-                       a.state_indices, a.num_slots);
+                       a.state_indices, a.num_slots, a.qk_norm ? 1 : 0);
     prof::end(stream);
     return hipGetLastError();
 }

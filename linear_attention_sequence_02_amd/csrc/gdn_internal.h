@@ -8,6 +8,8 @@
 namespace gdn {
 
 constexpr int kChunk = 64;   // prefill chunk length (tokens)
+// In-kernel q/k normalisation: x / sqrt(sum(x^2) + kQkNormEps) per token and head.
+constexpr float kQkNormEps = 1e-6f;
 
 struct DecodeArgs {
     const void* q;
@@ -21,6 +23,7 @@ struct DecodeArgs {
     int32_t num_slots;              // rows in the state pool (with state_indices)
     int32_t num_tokens = 1;         // tokens per sequence (multi-token step)
     float* token_states = nullptr;  // multi-token step: state after every token, or null
+    bool qk_norm = false;           // L2-normalise q and k in the kernel
     int32_t num_seqs, num_qk_heads, num_v_heads, d;
     float scale;
     bool bf16;
@@ -38,6 +41,7 @@ struct PrefillArgs {
     const int32_t* state_indices; // null: sequence n uses state row n; else row state_indices[n]
     const int32_t* has_initial;   // null: every sequence reads its initial state row (if any)
     int32_t num_slots;            // rows in the state pool (with state_indices)
+    bool qk_norm = false;         // L2-normalise q and k in the kernel
     void* out;
     void* workspace;
     size_t workspace_bytes;

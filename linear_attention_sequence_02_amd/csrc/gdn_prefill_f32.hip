@@ -43,7 +43,7 @@ __global__ __launch_bounds__(2 * D) void prefill_f32_kernel(
     const float* initial_state, const int32_t* __restrict__ cu_seqlens, float* final_state,
     float* __restrict__ out, int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads,
     float scale, const int32_t* __restrict__ state_indices, const int32_t* __restrict__ has_initial,
-    int32_t num_slots) {
+    int32_t num_slots, int32_t qk_norm) {
     constexpr int NT = 2 * D;
     constexpr int H = D / 2;   // key columns per thread
     __shared__ F32Smem<D> sm;
@@ -84,6 +84,17 @@ __global__ __launch_bounds__(2 * D) void prefill_f32_kernel(
             sm.bet[r] = in ? beta[(c0 + r) * num_v_heads + h] : 0.f;
         }
         __syncthreads();
+        if (qk_norm) {
+            // In-kernel L2 normalisation of every k and q row (rows past the end stay zero).
+            for (int r = tid; r < 2 * kChunk; r += NT) {
+                float* row = (r < kChunk) ? sm.K[r] : sm.Q[r - kChunk];
+                float ss = 0.f;
+                for (int j = 0; j < D; ++j) ss = fmaf(row[j], row[j], ss);
+                const float f = rsqrtf(ss + kQkNormEps);
+                for (int j = 0; j < D; ++j) row[j] *= f;
+            }
+            __syncthreads();
+        }
         // Phase 1: in-chunk cumulative decay.
         for (int r = tid; r < kChunk; r += NT) {
             float acc = 0.f;
@@ -183,7 +194,8 @@ static hipError_t launch_f32_t(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_f32_kernel<D>), dim3((unsigned)blocks), dim3(2 * D), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, a.g, a.beta,
                        a.initial_state, a.cu_seqlens, a.final_state, (float*)a.out, a.total_tokens,
-                       a.num_qk_heads, a.num_v_heads, a.scale, a.state_indices, a.has_initial, a.num_slots);
+                       a.num_qk_heads, a.num_v_heads, a.scale, a.state_indices, a.has_initial, a.num_slots,
+                       a.qk_norm ? 1 : 0);
     prof::end(stream);
     return hipGetLastError();
 }

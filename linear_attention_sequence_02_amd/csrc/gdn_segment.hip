@@ -154,15 +154,35 @@ __device__ __forceinline__ void prod_fetch_gb(ProdRegs& pr, const float* gc, con
     pr.b = __builtin_bit_cast(float, buf_ld_b32(chunk_rsrc(uniform_ptr(bc), (int64_t)nc * hv * 4), off));
 }
 
+// In-kernel L2 normalisation of one 8-element piece of a k or q row: the 16
+// consecutive lanes that hold the row sum their squares, and each element is
+// scaled and rounded back to bf16 (a zero row stays zero).
+__device__ __forceinline__ u32x4 l2norm_piece(u32x4 x) {
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = __uint_as_float(x[j] << 16);
+        f[2 * j + 1] = __uint_as_float(x[j] & 0xFFFF0000u);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf(f[j], f[j], ss);
+    const float r = rsqrtf(group_sum<16>(ss) + kQkNormEps);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = pack_bf16(f[2 * j] * r, f[2 * j + 1] * r);
+    return x;
+}
+
 // Rows past the end of a partial chunk were read as zero.
 template <int MODE>
-__device__ __forceinline__ void prod_stage_kq(SegSmem<MODE>& sm, int buf, const ProdRegs& pr, int pl) {
+__device__ __forceinline__ void prod_stage_kq(SegSmem<MODE>& sm, int buf, const ProdRegs& pr, int pl, bool qk_norm) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int p = pl + 256 * i;
         const int row = p >> 4, c8 = p & 15;
-        *reinterpret_cast<u32x4*>(&sm.K[buf][row][c8 * 8]) = pr.k[i];
-        if (MODE == kModeOut) *reinterpret_cast<u32x4*>(&sm.Q[buf][row][c8 * 8]) = pr.q[i];
+        *reinterpret_cast<u32x4*>(&sm.K[buf][row][c8 * 8]) = qk_norm ? l2norm_piece(pr.k[i]) : pr.k[i];
+        if (MODE == kModeOut)
+            *reinterpret_cast<u32x4*>(&sm.Q[buf][row][c8 * 8]) = qk_norm ? l2norm_piece(pr.q[i]) : pr.q[i];
     }
 }
 
@@ -592,6 +612,7 @@ struct SegArgs {
     int32_t num_slots;
     int32_t num_qk_heads, num_v_heads;
     float scale;
+    bool qk_norm;                   // L2-normalise k and q rows as they are staged
 };
 
 template <int MODE>
@@ -641,9 +662,9 @@ __device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A
         if (nchunks > 0) {
             fetch_kq(c_begin);
             fetch_gb(c_begin);
-            prod_stage_kq<MODE>(sm, 0, pr, pl);
+            prod_stage_kq<MODE>(sm, 0, pr, pl, A.qk_norm);
             fetch_kq(clampc(c_begin + 1));
-            if (nchunks > 1) prod_stage_kq<MODE>(sm, 1, pr, pl);
+            if (nchunks > 1) prod_stage_kq<MODE>(sm, 1, pr, pl, A.qk_norm);
         }
         lds_barrier();
         if (nchunks > 0) {
@@ -659,7 +680,7 @@ __device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A
             if (i + 1 < nchunks)
                 prod_factors<MODE>(sm, (int)((i + 1) % 3), sm.F[(i + 1) & 1], pr, chunk_nc(c + 1), scale, pw,
                                    lane);
-            if (i + 2 < nchunks) prod_stage_kq<MODE>(sm, (int)((i + 2) % 3), pr, pl);
+            if (i + 2 < nchunks) prod_stage_kq<MODE>(sm, (int)((i + 2) % 3), pr, pl, A.qk_norm);
             fetch_kq(clampc(c + 3));
             fetch_gb(clampc(c + 2));
             lds_barrier();
@@ -735,7 +756,8 @@ __global__ __launch_bounds__(64 * (4 + kProd)) void segment_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, const float* initial_state,
     const int32_t* __restrict__ cu, float* final_state, uint16_t* __restrict__ out, float* __restrict__ segws,
     int64_t total_tokens, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads, int32_t L, int64_t num_segs,
-    float scale, int32_t phase, const int32_t* state_indices, const int32_t* has_initial, int32_t num_slots) {
+    float scale, int32_t phase, const int32_t* state_indices, const int32_t* has_initial, int32_t num_slots,
+    int32_t qk_norm) {
     __shared__ SegSmem<kModeOut> sm;
 
     // XCD-aware placement: workgroups are dealt round-robin to the 8 XCDs
@@ -761,7 +783,7 @@ __global__ __launch_bounds__(64 * (4 + kProd)) void segment_kernel(
     tk.c_end = (tk.c_begin + L < nch) ? tk.c_begin + L : nch;
     tk.nchunks = tk.c_end - tk.c_begin;
     const SegArgs A = {q, k, v, g, beta, initial_state, final_state, out, segws, state_indices, has_initial,
-                       num_slots, num_qk_heads, num_v_heads, scale};
+                       num_slots, num_qk_heads, num_v_heads, scale, qk_norm != 0};
     if (phase == 0) {
         if (tk.j == 0) segment_body<kModeOut>(sm, A, tk);
         else if (tk.j < tk.nseg - 1) segment_body<kModeHM>(*reinterpret_cast<SegSmem<kModeHM>*>(&sm), A, tk);
@@ -903,7 +925,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(segment_kernel, grid, dim3(64 * (4 + kProd)), 0, stream, q, k, v, a.g, a.beta, a.initial_state,
                        a.cu_seqlens, a.final_state, (uint16_t*)a.out, seg_ws, a.total_tokens, a.num_seqs,
                        a.num_qk_heads, a.num_v_heads, L, segs, a.scale, 0, a.state_indices, a.has_initial,
-                       a.num_slots);
+                       a.num_slots, a.qk_norm ? 1 : 0);
     prof::end(stream);
     if (multi) {
         prof::begin(stream, "gdn_segment_combine");
@@ -914,7 +936,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(segment_kernel, grid, dim3(64 * (4 + kProd)), 0, stream, q, k, v, a.g, a.beta,
                            a.initial_state, a.cu_seqlens, a.final_state, (uint16_t*)a.out, seg_ws, a.total_tokens,
                            a.num_seqs, a.num_qk_heads, a.num_v_heads, L, segs, a.scale, 1, a.state_indices,
-                           a.has_initial, a.num_slots);
+                           a.has_initial, a.num_slots, a.qk_norm ? 1 : 0);
         prof::end(stream);
     }
     return hipGetLastError();

@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert set(declared_functions()) == {"gdn_prefill_workspace_size", "gdn_prefill_segment_chunks", "gdn_prefill",
                                          "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots",
-                                         "gdn_decode_multi",
+                                         "gdn_decode_multi", "gdn_prefill_ex", "gdn_decode_ex",
                                          "gdn_status_string", "gdn_build_info", "gdn_profile_start",
                                          "gdn_profile_stop"}
 
@@ -181,6 +181,19 @@ def test_decode_multi_rejects(lib, over, status):
 
 def test_decode_multi_with_no_sequences_is_a_no_op(lib):
     assert _decode_multi(lib, n=0) == gdn.GDN_OK
+
+
+def test_unknown_flags_are_rejected(lib):
+    st = lib.gdn_prefill_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, FAKE, 2, 100, 16, 32, 128, 128,
+                            1.0, gdn.GDN_BF16, 0x2, FAKE, FAKE, 1 << 40, None)
+    assert st == gdn.GDN_ERR_INVALID_ARG
+    st = lib.gdn_decode_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 1, 16, 32, 128, 128, 1.0, gdn.GDN_BF16,
+                           0x80000000, FAKE, None, None)
+    assert st == gdn.GDN_ERR_INVALID_ARG
+    # the general decode keeps the token-count checks of gdn_decode_multi
+    st = lib.gdn_decode_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 0, 16, 32, 128, 128, 1.0, gdn.GDN_BF16,
+                           gdn.GDN_FLAG_QK_L2NORM, FAKE, None, None)
+    assert st == gdn.GDN_ERR_INVALID_ARG
 
 
 def _prefill_slots(lib, **over):
