@@ -35,12 +35,12 @@ namespace gdn {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool QKN>
 __global__ __launch_bounds__(512) void decode_step_kernel(
     const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
     int32_t num_qk_heads, int32_t num_v_heads, float scale, void* __restrict__ out_,
-    const int32_t* __restrict__ state_indices, int32_t num_slots, int32_t qk_norm) {
+    const int32_t* __restrict__ state_indices, int32_t num_slots) {
     constexpr int L = D / 16;                    // lanes per state row (16 floats each)
     constexpr int NT = (D * L < 512) ? D * L : 512;
     constexpr int ROWS_PER_PASS = NT / L;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
     // In-kernel L2 normalisation: k and q enter through the factors rk, rq
     // (1 when off: every product below is then exactly the plain one).
     float rk = 1.f, rq = 1.f;
-    if (qk_norm) {
+    if constexpr (QKN) {
         float nk = 0.f, nq = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -170,13 +170,12 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
 // once; optionally the state after every token is stored as well, so that a
 // caller can resume from the last accepted token. Inputs are token-major per
 // sequence: token t of sequence n is row n * num_tokens + t.
-template <int D, bool BF16>
+template <int D, bool BF16, bool QKN>
 __global__ __launch_bounds__(512) void decode_multi_kernel(
     const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state, int32_t num_tokens,
     int32_t num_qk_heads, int32_t num_v_heads, float scale, void* __restrict__ out_,
-    float* __restrict__ token_states, const int32_t* __restrict__ state_indices, int32_t num_slots,
-    int32_t qk_norm) {
+    float* __restrict__ token_states, const int32_t* __restrict__ state_indices, int32_t num_slots) {
     constexpr int L = D / 16;
     constexpr int NT = (D * L < 512) ? D * L : 512;
     constexpr int ROWS_PER_PASS = NT / L;
@@ -267,7 +266,7 @@ __global__ __launch_bounds__(512) void decode_multi_kernel(
         };
         const float alpha = exp_nonpos(cur.g);
         float rk = 1.f, rq = 1.f;   // in-kernel L2 normalisation factors (1 when off)
-        if (qk_norm) {
+        if constexpr (QKN) {
             float nk = 0.f, nq = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -328,50 +327,60 @@ __global__ __launch_bounds__(512) void decode_multi_kernel(
             __builtin_nontemporal_store(s[m][i], &S[(r0 + m * ROWS_PER_PASS) * (D / 4) + c + L * i]);
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool QKN>
 static hipError_t launch_decode_multi_t(const DecodeArgs& a, hipStream_t stream) {
     constexpr int L = D / 16;
     constexpr int NT = (D * L < 512) ? D * L : 512;
     const int64_t blocks = (int64_t)a.num_seqs * a.num_v_heads;
     prof::begin(stream, "gdn_decode_multi");
-    hipLaunchKernelGGL((decode_multi_kernel<D, BF16>), dim3((unsigned)blocks), dim3(NT), 0, stream,
+    hipLaunchKernelGGL((decode_multi_kernel<D, BF16, QKN>), dim3((unsigned)blocks), dim3(NT), 0, stream,
                        a.q, a.k, a.v, a.g, a.beta, a.state, a.num_tokens, a.num_qk_heads, a.num_v_heads, a.scale,
-                       a.out, a.token_states, a.state_indices, a.num_slots, a.qk_norm ? 1 : 0);
+                       a.out, a.token_states, a.state_indices, a.num_slots);
     prof::end(stream);
     return hipGetLastError();
+}
+
+template <int D, bool BF16>
+static hipError_t launch_decode_multi_n(const DecodeArgs& a, hipStream_t stream) {
+    return a.qk_norm ? launch_decode_multi_t<D, BF16, true>(a, stream) : launch_decode_multi_t<D, BF16, false>(a, stream);
 }
 
 hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t stream) {
     const bool bf = a.bf16;
     switch (a.d) {
-        case 16: return bf ? launch_decode_multi_t<16, true>(a, stream) : launch_decode_multi_t<16, false>(a, stream);
-        case 32: return bf ? launch_decode_multi_t<32, true>(a, stream) : launch_decode_multi_t<32, false>(a, stream);
-        case 64: return bf ? launch_decode_multi_t<64, true>(a, stream) : launch_decode_multi_t<64, false>(a, stream);
-        case 128: return bf ? launch_decode_multi_t<128, true>(a, stream) : launch_decode_multi_t<128, false>(a, stream);
+        case 16: return bf ? launch_decode_multi_n<16, true>(a, stream) : launch_decode_multi_n<16, false>(a, stream);
+        case 32: return bf ? launch_decode_multi_n<32, true>(a, stream) : launch_decode_multi_n<32, false>(a, stream);
+        case 64: return bf ? launch_decode_multi_n<64, true>(a, stream) : launch_decode_multi_n<64, false>(a, stream);
+        case 128: return bf ? launch_decode_multi_n<128, true>(a, stream) : launch_decode_multi_n<128, false>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool QKN>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     constexpr int L = D / 16;
     constexpr int NT = (D * L < 512) ? D * L : 512;
     const int64_t blocks = (int64_t)a.num_seqs * a.num_v_heads;
     prof::begin(stream, "gdn_decode_step");
-    hipLaunchKernelGGL((decode_step_kernel<D, BF16>), dim3((unsigned)blocks), dim3(NT), 0, stream,
+    hipLaunchKernelGGL((decode_step_kernel<D, BF16, QKN>), dim3((unsigned)blocks), dim3(NT), 0, stream,
                        a.q, a.k, a.v, a.g, a.beta, a.state, a.num_qk_heads, a.num_v_heads, a.scale, a.out,
-                       a.state_indices, a.num_slots, a.qk_norm ? 1 : 0);
+                       a.state_indices, a.num_slots);
     prof::end(stream);
     return hipGetLastError();
+}
+
+template <int D, bool BF16>
+static hipError_t launch_decode_n(const DecodeArgs& a, hipStream_t stream) {
+    return a.qk_norm ? launch_decode_t<D, BF16, true>(a, stream) : launch_decode_t<D, BF16, false>(a, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const bool bf = a.bf16;
     switch (a.d) {
-        case 16: return bf ? launch_decode_t<16, true>(a, stream) : launch_decode_t<16, false>(a, stream);
-        case 32: return bf ? launch_decode_t<32, true>(a, stream) : launch_decode_t<32, false>(a, stream);
-        case 64: return bf ? launch_decode_t<64, true>(a, stream) : launch_decode_t<64, false>(a, stream);
-        case 128: return bf ? launch_decode_t<128, true>(a, stream) : launch_decode_t<128, false>(a, stream);
+        case 16: return bf ? launch_decode_n<16, true>(a, stream) : launch_decode_n<16, false>(a, stream);
+        case 32: return bf ? launch_decode_n<32, true>(a, stream) : launch_decode_n<32, false>(a, stream);
+        case 64: return bf ? launch_decode_n<64, true>(a, stream) : launch_decode_n<64, false>(a, stream);
+        case 128: return bf ? launch_decode_n<128, true>(a, stream) : launch_decode_n<128, false>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
