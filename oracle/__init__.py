@@ -21,6 +21,8 @@ flash-linear-attention kernels), are normalised here first, per token and
 head, as x / sqrt(sum(x^2) + 1e-6) in fp64 (the epsilon is this library's
 reading; the pages give none).
 
+  backward(...)   fp64 gradients of the recurrence (backward.py: the rule written with
+                  PyTorch CPU ops in float64, reversed by torch.autograd).
   upcast(x)       exact fp64 value of a bf16-bit / fp32 / fp64 array.
   qk_normalize(x) that normalisation along the last axis, fp64.
 """
@@ -148,3 +150,4 @@ def rel_l2(x, ref) -> float:
 
 
 from .chunked import chunked  # noqa: E402,F401
+from .backward import backward  # noqa: E402,F401
