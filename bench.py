@@ -24,6 +24,9 @@ Roofline figures use algorithmic work only:
   multi-token decode ("decode_multi"): 4 tokens per sequence from one state,
       256 sequences: the state read and written once plus 4 tokens' inputs and
       outputs, 1,099,169,792 bytes per step
+  backward ("backward"): gradients of the prefill on the T = 4096 layer shape,
+      against the fp32 vector peak (157.3 TFLOP/s) at 17 d^2 flop per token and
+      V head (the recomputation of forward states not counted)
   with q and k L2-normalised in the kernels ("prefill_qk_l2norm",
       "decode.qk_l2norm"): the same inputs and algorithmic work
 Peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8.0 TB/s.
@@ -60,6 +63,11 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 PREFILL_FLOP_PER_TOKEN = 4_194_304
 PREFILL_BYTES_PER_TOKEN = 24_832
+PEAK_FP32_VECTOR_TFLOPS = 157.3
+# Backward, per token over all 32 V heads (d = 128): the reverse step's products with the state
+# (S k, dS update by do q^T, dS k, S^T do, dS^T u and S^T du, <dS, S>, the dS recurrence) at
+# 17 d^2 flop per V head; the recomputation of the forward states is the implementation's own.
+BACKWARD_FLOP_PER_TOKEN = 17 * 128 * 128 * 32
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"gdn_segment_out": "gdn_segment.hip", "gdn_segment_maps": "gdn_segment.hip",
                   "gdn_decode_step": "gdn_decode.hip", "gdn_decode_multi": "gdn_decode.hip"}
@@ -214,6 +222,7 @@ def main():
     ap.add_argument("--decode-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one 256 MiB device-to-device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -393,6 +402,29 @@ def main():
                                                "traffic": recorded_traffic("gdn_decode_multi", ym.name)}}
         log(f"[bench] multi-token decode {mms:.3f} ms/step, {mgbs:.1f} GB/s")
         del dm, stm, om
+
+    if not args.no_backward:
+        # Backward of the prefill on the 4,096-token Qwen3-Next layer shape (bf16 inputs, fp32 gradients).
+        xb = I.qwen3_next_prefill(T=4096)
+        db = to_device(xb, dev)
+        gout = torch.from_numpy(I.draw(T=4096, hqk=xb.hqk, hv=xb.hv, dk=xb.dk, seed=1007).v).view(torch.bfloat16).to(dev)
+        wsb = torch.empty(gdn.gdn_backward_workspace_size(xb.T, 1, xb.hqk, xb.hv, xb.dk, xb.dv, gdn.GDN_BF16),
+                          dtype=torch.uint8, device=dev)
+
+        def backward():
+            gdn.gdn_backward(db["q"], db["k"], db["v"], db["g"], db["beta"], gout, None, None, workspace=wsb)
+
+        bsteps = max(2, args.steps // 4)
+        bms, bkern = time_calls(backward, bsteps, 2, torch)
+        bkms = bkern.get("gdn_backward", (0, bms))[1]
+        btf = BACKWARD_FLOP_PER_TOKEN * xb.T / (bkms / 1e3) / 1e12
+        result["backward"] = {"workload": "qwen3next_gdn_backward_T4096", "steps": bsteps, "ms_per_step": bms,
+                              "kernel_ms_per_launch": bkms, "tokens_per_s": xb.T / (bms / 1e3),
+                              "roofline": {"kernel": "gdn_backward", "bound": "alu", "achieved": btf,
+                                           "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                                           "frac": btf / PEAK_FP32_VECTOR_TFLOPS}}
+        log(f"[bench] backward {bms:.3f} ms/step")
+        del db, gout, wsb
 
     if args.calibration_copy:
         a_ = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

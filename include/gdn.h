@@ -262,6 +262,38 @@ gdn_status_t gdn_decode_ex(const void* q, const void* k, const void* v,
                            void* out, float* token_states, void* stream);
 
 /*
+ * Backward of the prefill (for training; page "Qwen3-Next-80B-A3B-Instruct",
+ * section "Highlights", on the hybrid layout's training efficiency): the
+ * gradients of the recurrence with respect to q, k, v, g, beta and the initial
+ * states, given the gradient of the outputs and, optionally, of the final
+ * states. Inputs and shapes as for gdn_prefill (flags 0: q and k unit-length);
+ *   d_out           [total_tokens, num_v_heads, d_v]    dtype of q
+ *   d_final_state   [num_seqs, num_v_heads, d_v, d_k]   float, or NULL (zeros)
+ * Outputs, all float, written:
+ *   dq, dk          [total_tokens, num_qk_heads, d_k]   (summed over the V heads of a QK head)
+ *   dv              [total_tokens, num_v_heads, d_v]
+ *   dg, dbeta       [total_tokens, num_v_heads]         (dg: with respect to g = log alpha)
+ *   d_initial_state [num_seqs, num_v_heads, d_v, d_k], or NULL
+ * The computation is token by token in fp32 (a reference-grade path, not tuned
+ * for speed): one workgroup per (sequence, V head) keeps a checkpoint of the
+ * state every 16 tokens in the workspace and rebuilds the state before each
+ * token from it. workspace: gdn_backward_workspace_size(...) bytes.
+ */
+size_t gdn_backward_workspace_size(int64_t total_tokens, int32_t num_seqs,
+                                   int32_t num_qk_heads, int32_t num_v_heads,
+                                   int32_t d_k, int32_t d_v, gdn_dtype_t dtype);
+gdn_status_t gdn_backward(const void* q, const void* k, const void* v,
+                          const float* g, const float* beta,
+                          const float* initial_state,
+                          const int32_t* cu_seqlens, int32_t num_seqs,
+                          int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads,
+                          int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype,
+                          const void* d_out, const float* d_final_state,
+                          float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                          float* d_initial_state,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Instrumentation (for benchmarks and profiling; process-global, not
  * thread-safe, not for graph capture). After gdn_profile_start(), every kernel
  * the library launches is bracketed by a pair of HIP events recorded on the

@@ -15,7 +15,7 @@ import threading
 import torch
 
 __all__ = ["gdn_prefill", "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots", "gdn_decode_multi",
-           "gdn_prefill_ex", "gdn_decode_ex", "GDN_FLAG_QK_L2NORM",
+           "gdn_prefill_ex", "gdn_decode_ex", "GDN_FLAG_QK_L2NORM", "gdn_backward", "gdn_backward_workspace_size",
            "gdn_prefill_workspace_size", "gdn_prefill_segment_chunks",
            "gdn_status_string",
            "gdn_build_info", "gdn_profile_start", "gdn_profile_stop", "GDN_BF16", "GDN_FP32", "GdnError", "library_path"]
@@ -59,6 +59,11 @@ def _load():
             lib.gdn_decode_step_slots.argtypes = [_vp] * 7 + [_i32] * 6 + [_f32, ctypes.c_int, _vp, _vp]
             lib.gdn_decode_multi.restype = ctypes.c_int
             lib.gdn_decode_multi.argtypes = [_vp] * 7 + [_i32] * 7 + [_f32, ctypes.c_int, _vp, _vp, _vp]
+            lib.gdn_backward_workspace_size.restype = _sz
+            lib.gdn_backward_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, ctypes.c_int]
+            lib.gdn_backward.restype = ctypes.c_int
+            lib.gdn_backward.argtypes = ([_vp] * 7 + [_i32, _i64, _i32, _i32, _i32, _i32, _f32, ctypes.c_int]
+                                         + [_vp] * 9 + [_sz, _vp])
             lib.gdn_prefill_ex.restype = ctypes.c_int
             lib.gdn_prefill_ex.argtypes = ([_vp] * 9 + [_i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                                        ctypes.c_int, ctypes.c_uint32, _vp, _vp, _sz, _vp])
@@ -379,3 +384,43 @@ def gdn_decode_ex(q, k, v, g, beta, state, *, num_tokens: int = 1, state_indices
     if st != GDN_OK:
         raise GdnError(st, "gdn_decode_ex")
     return out, token_states
+
+
+def gdn_backward_workspace_size(total_tokens: int, num_seqs: int, num_qk_heads: int, num_v_heads: int,
+                                d_k: int, d_v: int, dtype: int) -> int:
+    return int(_load().gdn_backward_workspace_size(total_tokens, num_seqs, num_qk_heads, num_v_heads, d_k, d_v,
+                                                   dtype))
+
+
+def gdn_backward(q, k, v, g, beta, d_out, initial_state=None, cu_seqlens=None, d_final_state=None, *,
+                 scale: float = 1.0, output_d_initial_state: bool = True, workspace=None, stream=None):
+    """Gradients of the prefill given d_out [T, Hv, d] (dtype of q) and optionally d_final_state
+    [N, Hv, d, d]. Returns a dict of fp32 tensors: dq, dk [T, Hqk, d], dv [T, Hv, d], dg, dbeta [T, Hv],
+    d_initial_state [N, Hv, d, d] (or None)."""
+    dev = q.device
+    _check(q, "q", device=dev)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("d_out", d_out)):
+        _check(t, name, q.dtype, dev)
+    for name, t in (("g", g), ("beta", beta), ("initial_state", initial_state), ("d_final_state", d_final_state)):
+        _check(t, name, torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    T, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    n = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    f32 = dict(dtype=torch.float32, device=dev)
+    res = {"dq": torch.empty((T, hqk, dk), **f32), "dk": torch.empty((T, hqk, dk), **f32),
+           "dv": torch.empty((T, hv, dv), **f32), "dg": torch.empty((T, hv), **f32),
+           "dbeta": torch.empty((T, hv), **f32),
+           "d_initial_state": torch.empty((n, hv, dv, dk), **f32) if output_d_initial_state else None}
+    need = gdn_backward_workspace_size(T, n, hqk, hv, dk, dv, dt)
+    if workspace is None:
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _load().gdn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+                              n, T, hqk, hv, dk, dv, float(scale), dt, _ptr(d_out), _ptr(d_final_state),
+                              _ptr(res["dq"]), _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dg"]), _ptr(res["dbeta"]),
+                              _ptr(res["d_initial_state"]), _ptr(workspace), ws_bytes, _stream(stream, dev))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_backward")
+    return res

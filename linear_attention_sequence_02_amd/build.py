@@ -8,7 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_prefill_f32.hip", "gdn_segment.hip", "gdn_profile.hip"]
+SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_prefill_f32.hip", "gdn_segment.hip", "gdn_profile.hip",
+           "gdn_backward.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for every HIP file (the compiler would

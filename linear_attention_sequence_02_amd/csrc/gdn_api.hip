@@ -213,6 +213,42 @@ gdn_status_t gdn_decode_step_slots(const void* q, const void* k, const void* v, 
                        out, stream, state_indices, num_slots);
 }
 
+size_t gdn_backward_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t num_qk_heads,
+                                   int32_t num_v_heads, int32_t d_k, int32_t d_v, gdn_dtype_t dtype) {
+    if (total_tokens < 0 || num_seqs < 0) return 0;
+    if (num_qk_heads <= 0 || num_v_heads <= 0 || num_v_heads % num_qk_heads != 0) return 0;
+    if ((dtype != GDN_BF16 && dtype != GDN_FP32) || d_k != d_v || !fp32_head_size_ok(d_k)) return 0;
+    return gdn::backward_workspace_bytes(total_tokens, num_seqs, num_v_heads, d_k);
+}
+
+gdn_status_t gdn_backward(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                          int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k, int32_t d_v,
+                          float scale, gdn_dtype_t dtype, const void* d_out, const float* d_final_state, float* dq,
+                          float* dk, float* dv, float* dg, float* dbeta, float* d_initial_state, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (num_qk_heads <= 0 || num_v_heads <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_INVALID_ARG;
+    if (num_v_heads % num_qk_heads != 0) return GDN_ERR_INVALID_ARG;
+    if (dtype != GDN_BF16 && dtype != GDN_FP32) return GDN_ERR_INVALID_ARG;
+    if (d_k != d_v || !fp32_head_size_ok(d_k)) return GDN_ERR_UNSUPPORTED;
+    if (total_tokens < 0 || num_seqs < 0) return GDN_ERR_INVALID_ARG;
+    if (total_tokens > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    if (cu_seqlens == nullptr && num_seqs != 1) return GDN_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !d_out || !dq || !dk || !dv || !dg || !dbeta))
+        return GDN_ERR_INVALID_ARG;
+    if (num_seqs == 0) return GDN_OK;
+    const size_t need = gdn_backward_workspace_size(total_tokens, num_seqs, num_qk_heads, num_v_heads, d_k, d_v,
+                                                    dtype);
+    if (workspace == nullptr || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+    gdn::BackwardArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.initial_state = initial_state; a.cu_seqlens = cu_seqlens;
+    a.d_out = d_out; a.d_final_state = d_final_state; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta;
+    a.d_initial_state = d_initial_state; a.workspace = workspace; a.total_tokens = total_tokens;
+    a.num_seqs = num_seqs; a.num_qk_heads = num_qk_heads; a.num_v_heads = num_v_heads; a.d = d_k; a.scale = scale;
+    a.bf16 = (dtype == GDN_BF16);
+    return hip_status(gdn::launch_backward(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* gdn_status_string(gdn_status_t s) {
     switch (s) {
         case GDN_OK: return "GDN_OK";

@@ -60,6 +60,29 @@ __device__ __forceinline__ int64_t state_row(const int32_t* state_indices, int32
     return (s >= 0 && s < num_slots) ? s : -1;
 }
 
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* initial_state;   // may be null (zeros)
+    const int32_t* cu_seqlens;    // may be null (one sequence)
+    const void* d_out;            // [T, Hv, d], the dtype of q
+    const float* d_final_state;   // may be null (zeros)
+    float* dq;                    // [T, Hqk, d]
+    float* dk;                    // [T, Hqk, d]
+    float* dv;                    // [T, Hv, d]
+    float* dg;                    // [T, Hv]
+    float* dbeta;                 // [T, Hv]
+    float* d_initial_state;       // may be null
+    void* workspace;
+    int64_t total_tokens;
+    int32_t num_seqs, num_qk_heads, num_v_heads, d;
+    float scale;
+    bool bf16;
+};
+
 namespace prof {
 // Event pair around one kernel launch when instrumentation is on (no-op otherwise).
 void begin(hipStream_t s, const char* name);
@@ -67,6 +90,8 @@ void end(hipStream_t s);
 }  // namespace prof
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
+size_t backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_v_heads, int32_t d);
 hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);

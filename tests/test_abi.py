@@ -32,6 +32,7 @@ def test_header_declares_the_entry_points():
     assert set(declared_functions()) == {"gdn_prefill_workspace_size", "gdn_prefill_segment_chunks", "gdn_prefill",
                                          "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots",
                                          "gdn_decode_multi", "gdn_prefill_ex", "gdn_decode_ex",
+                                         "gdn_backward", "gdn_backward_workspace_size",
                                          "gdn_status_string", "gdn_build_info", "gdn_profile_start",
                                          "gdn_profile_stop"}
 
@@ -194,6 +195,37 @@ def test_unknown_flags_are_rejected(lib):
     st = lib.gdn_decode_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 0, 16, 32, 128, 128, 1.0, gdn.GDN_BF16,
                            gdn.GDN_FLAG_QK_L2NORM, FAKE, None, None)
     assert st == gdn.GDN_ERR_INVALID_ARG
+
+
+def _backward(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, cu=FAKE, n=2, T=100, hqk=16, hv=32, dk=128, dv=128,
+             scale=1.0, dt=gdn.GDN_BF16, dout=FAKE, dfin=None, dq=FAKE, dkk=FAKE, dvv=FAKE, dg=FAKE, db=FAKE,
+             dinit=None, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(over)
+    return lib.gdn_backward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["n"], a["T"], a["hqk"],
+                            a["hv"], a["dk"], a["dv"], a["scale"], a["dt"], a["dout"], a["dfin"], a["dq"], a["dkk"],
+                            a["dvv"], a["dg"], a["db"], a["dinit"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(hqk=3), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dout=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dq=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(T=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(cu=None, n=2), gdn.GDN_ERR_INVALID_ARG),
+    (dict(dk=100, dv=100), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(ws=None), gdn.GDN_ERR_WORKSPACE),
+    (dict(wsb=1024), gdn.GDN_ERR_WORKSPACE),
+])
+def test_backward_rejects(lib, over, status):
+    assert _backward(lib, **over) == status
+
+
+def test_backward_workspace_size(lib):
+    ws = gdn.gdn_backward_workspace_size
+    # a checkpoint per 16 tokens (plus one per sequence) and per-V-head q/k gradient parts
+    assert ws(4096, 1, 16, 32, 128, 128, gdn.GDN_BF16) == (4096 // 16 + 1) * 32 * 128 * 128 * 4 + 2 * 4096 * 32 * 128 * 4
+    assert ws(100, 1, 3, 32, 128, 128, gdn.GDN_BF16) == 0
 
 
 def _prefill_slots(lib, **over):

@@ -1,0 +1,48 @@
+"""Backward of the prefill (gdn_backward) against the fp64 oracle's gradients (PyTorch CPU
+autograd of the recurrence, itself pinned by finite differences). The GPU computes the gradients
+in fp32 from inputs that are exact in fp32 (bf16 inputs widen exactly), so every gradient is held
+to the fp32 bar, relative L2 <= 1e-4 per tensor."""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_sequence_02_amd as gdn
+import oracle
+from synth import inputs as I
+from tests.gpu_util import log, rel_l2, to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+@pytest.mark.parametrize("dtype,d,lengths,with_dfinal", [
+    ("fp32", 16, [37, 0, 70, 16], True),
+    ("fp32", 32, [50, 19], False),
+    ("fp32", 64, [33, 48], True),
+    ("bf16", 128, [45, 20], True),
+    ("bf16", 128, [81], False),
+])
+def test_backward(dtype, d, lengths, with_dfinal):
+    x = I.draw(lengths=lengths, hqk=1 if d == 128 else 2, hv=2 if d == 128 else 4, dk=d, dtype=dtype,
+               seed=400 + d + len(lengths), s0_std=0.3, scale=0.5, name=f"backward_{dtype}_d{d}")
+    rng = np.random.default_rng(401 + d)
+    d_out = rng.standard_normal(x.v.shape).astype(np.float32)
+    d_fin = rng.standard_normal(x.s0.shape).astype(np.float32) if with_dfinal else None
+    if dtype == "bf16":   # d_out in the inputs' dtype: round to bf16 bits
+        d_out_in = I.f32_to_bf16_bits(d_out)
+        d_out = oracle.upcast(d_out_in)
+        dev_dout = torch.from_numpy(d_out_in).view(torch.bfloat16).cuda()
+    else:
+        dev_dout = torch.from_numpy(d_out).cuda()
+    dev = to_device(x)
+    log(f"[gpu] gdn_backward {x.name} T={x.T} lengths={lengths}")
+    res = gdn.gdn_backward(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev_dout, dev["s0"], dev["cu"],
+                           None if d_fin is None else torch.from_numpy(d_fin).cuda(), scale=x.scale)
+    torch.cuda.synchronize()
+    ref = oracle.backward(x.q, x.k, x.v, x.g, x.beta, x.s0, x.cu_seqlens, d_out, d_fin, scale=x.scale)
+    pairs = [("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dg", "dg"), ("dbeta", "dbeta"), ("d_initial_state", "ds0")]
+    for mine, theirs in pairs:
+        e = rel_l2(res[mine].cpu().numpy(), ref[theirs])
+        log(f"[parity] {x.name} {mine}: rel={e:.3e}")
+        assert e <= TOL, (mine, e)
