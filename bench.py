@@ -416,11 +416,15 @@ def main():
 
         bsteps = max(2, args.steps // 4)
         bms, bkern = time_calls(backward, bsteps, 2, torch)
-        bkms = bkern.get("gdn_backward", (0, bms))[1]
+        # three stages per call: the two scans, the per-interval gradients, the fixed-order sums
+        bparts = {k: bkern[k][1] for k in ("gdn_backward_scan", "gdn_backward_grad", "gdn_backward_sums")
+                  if k in bkern}
+        bkms = sum(bparts.values()) or bms
         btf = BACKWARD_FLOP_PER_TOKEN * xb.T / (bkms / 1e3) / 1e12
         result["backward"] = {"workload": "qwen3next_gdn_backward_T4096", "steps": bsteps, "ms_per_step": bms,
-                              "kernel_ms_per_launch": bkms, "tokens_per_s": xb.T / (bms / 1e3),
-                              "roofline": {"kernel": "gdn_backward", "bound": "alu", "achieved": btf,
+                              "kernel_ms_per_launch": bparts, "tokens_per_s": xb.T / (bms / 1e3),
+                              "roofline": {"kernel": "gdn_backward_scan+grad+sums", "bound": "alu",
+                                           "achieved": btf,
                                            "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
                                            "frac": btf / PEAK_FP32_VECTOR_TFLOPS}}
         log(f"[bench] backward {bms:.3f} ms/step")

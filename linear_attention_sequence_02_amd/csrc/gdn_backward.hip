@@ -321,22 +321,60 @@ __global__ __launch_bounds__(BwdShape<D>::NT) void backward_scan_kernel(
     }
 }
 
-// Pass 2: block (slot, V head, row block); slots outside every sequence's range exit.
-// The four tokens of a sub-block share one round of cross-wave sums.
+// Pass 2, one workgroup (4 waves) per (interval, V head): the interval as a
+// chunk of 16 tokens (padded with g = 0, beta = 0 and zero inputs, which are
+// identity steps), entry state S0 and end gradient G from the scans. With
+// gamma the in-chunk cumulative sum of g, Gam = exp(gamma), Gp = exp(gamma_last
+// - gamma), dec[r][c] = exp(gamma_r - gamma_c), At = dec (K K^T) strictly below
+// the diagonal, A = diag(beta) At, P = dec (Q K^T) on and below it and
+// T = (I + A)^-1, the token rule unrolls to (rows are tokens):
+//   U  = T diag(beta) (V - diag(Gam) K S0^T)       AW = diag(Gam) K S0^T + At U
+//   dU = T^T (diag(Gp) K G^T + scale P^T dO)       (du_t = E_t k_t, E_t the state gradient)
+//   dv = diag(beta) dU,   dbeta_t = du_t . (v_t - AW_t)
+//   dQ = scale (diag(Gam) dO S0 + M4 K),           M4 = [tau <= t] dec (dO U^T)
+//   dK = diag(Gp) U G - diag(beta Gam) dU S0 + scale M4^T Q - M5 K,
+//        M5[t][s] = [s > t] dec[s][t] beta_s (dU U^T)[s][t] + [s < t] beta_t dec[t][s] (dU U^T)[t][s]
+//   dg_t = exp(gamma_last) <G, S0> + sum_{tau < t} a_tau + sum_{s >= t} b_s - sum_{s > t} c_s
+//          + sum_{s >= t, tau < t} scale P[s][tau] (dO U^T)[s][tau]
+//          - sum_{s > t, tau < t} A[s][tau] (dU U^T)[s][tau] - beta_t du_t . AW_t,
+//   a = Gp (U G . K), b = scale Gam (dO S0 . Q), c = Gam beta (dU S0 . K) (row dots).
+// Products over the value index (U G, dO S0, dU S0, dO U^T, dU U^T, <G, S0>) run
+// over blocks of 32 state rows staged in LDS and accumulate in registers. All
+// products are fp32 MFMA 16x16x4 (lane (g, m): A[m][k], B[k][m], D[4 g + e][m];
+// any fixed order of k serves, so long contractions take k = g (K / 4) + kk).
+template <int D>
+struct ChunkShape {
+    static constexpr int R = D < 32 ? D : 32;   // state rows per block
+    static constexpr int NB = D / R;            // blocks
+    static constexpr int KP = D + 4;            // fp32 row pitch of d-wide rows
+    static constexpr int BP = R + 4;            // fp32 row pitch of block-wide rows
+    static constexpr int NTD = D / 16;          // 16-column tiles over d
+    static constexpr int NTR = R / 16;          // 16-column tiles over a block
+    static constexpr int TPW = (NTD + 3) / 4;   // d tiles per wave
+};
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <int D, bool BF16>
-__global__ __launch_bounds__(BwdShape<D>::NT) void backward_grad_kernel(
-    BwdIn in, const float* __restrict__ ck_s, const float* __restrict__ ck_ds, float* __restrict__ dq_p,
-    float* __restrict__ dk_p, float* __restrict__ gb_p, float* __restrict__ dv) {
-    using Sh = BwdShape<D>;
-    using RB = RowBlock<D, BF16>;
-    constexpr int L = Sh::L, SPLIT = Sh::SPLIT, NT = Sh::NT, WL = Sh::WL, NW = Sh::NW;
-    __shared__ typename RB::Lds lds;
-    __shared__ __align__(16) float red[kSub][NW][2][D];
-    __shared__ __align__(16) float reds[kSub][NW][4];
-    const int split = blockIdx.x % SPLIT;
-    const int h = (blockIdx.x / SPLIT) % in.num_v_heads;
-    const int64_t sl = blockIdx.x / (SPLIT * in.num_v_heads);
-    // The sequence whose slots hold sl: the last n with ckpt_base(n) <= sl.
+__global__ __launch_bounds__(256) void backward_grad_kernel(
+    BwdIn in, const float* __restrict__ ck_s, const float* __restrict__ ck_ds, float* __restrict__ dq_h,
+    float* __restrict__ dk_h, float* __restrict__ dg, float* __restrict__ dbeta, float* __restrict__ dv) {
+    using CS = ChunkShape<D>;
+    constexpr int C = kCkpt, R = CS::R, NB = CS::NB, KP = CS::KP, BP = CS::BP, NTD = CS::NTD, NTR = CS::NTR,
+                  TPW = CS::TPW;
+    constexpr int SP = C + 1;   // pitch of the 16 x 16 matrices
+    static_assert(C == 16 && R % 16 == 0, "chunk of 16 tokens, blocks of whole tiles");
+    __shared__ __align__(16) float Kf[C][KP], Qf[C][KP];
+    __shared__ __align__(16) float Sb[R][KP], Gb[R][KP];
+    __shared__ float Vb[C][BP], dOb[C][BP], KSs[C][BP], KGs[C][BP], Us[C][BP], dUs[C][BP], Rs[C][BP];
+    __shared__ float At[C][SP], Pm[C][SP], Tm[C][SP], KK[C][SP], QK[C][SP], M4[C][SP], M5[C][SP], dOU[C][SP],
+        DUm[C][SP];
+    __shared__ float gin[C], gam[C], Gam[C], Gp[C], bet[C], part[4][3][C], red[4], dgs[C];
+
+    const int h = blockIdx.x % in.num_v_heads;
+    const int64_t sl = blockIdx.x / in.num_v_heads;
     int n = 0;
     if (in.cu) {
         int lo = 0, hi = in.num_seqs - 1;
@@ -349,152 +387,318 @@ __global__ __launch_bounds__(BwdShape<D>::NT) void backward_grad_kernel(
     }
     const int64_t bos = in.cu ? (int64_t)in.cu[n] : 0, eos = in.cu ? (int64_t)in.cu[n + 1] : in.total_tokens;
     const int64_t j = sl - ckpt_base(in.cu, n);
-    if (j < 0 || j >= (eos - bos + kCkpt - 1) / kCkpt) return;   // a gap slot: uniform over the block
-    RB rb(in, lds, h, split);
-    const int tid = threadIdx.x, c = rb.c, rl = rb.rl, row = rb.row, wv = tid / 64, ln = tid % 64;
+    if (j < 0 || j >= (eos - bos + C - 1) / C) return;   // a gap slot: uniform over the block
+    const int64_t t0 = bos + j * C;
+    const int cnt = (int)min((int64_t)C, eos - t0);
+    const int tid = threadIdx.x, w = tid / 64, ln = tid % 64, g4 = ln / 16, m = ln % 16;
+    const int hv = in.num_v_heads, hqk = in.num_qk_heads, hq = h / (hv / hqk);
     const float scale = in.scale;
-    const int64_t off = (sl * in.num_v_heads + h) * (int64_t)D * D;
-    const int64_t t0 = bos + j * kCkpt, t1 = (t0 + kCkpt < eos) ? t0 + kCkpt : eos;
-    const int cnt = (int)(t1 - t0);
-    {
-        typename RB::Fetch f;
-        rb.fetch(f, t0, t1, true, true, true);
-        rb.commit(f, true, true, true);
-    }
-    Row dS, sub[kCkpt / kSub];
-    rb.load_row(ck_ds + off, dS);
-    // The state at the start of every sub-block.
-    {
-        Row S;
-        rb.load_row(ck_s + off, S);
-#pragma unroll
-        for (int sb = 0; sb < kCkpt / kSub; ++sb) {
-            RB::copy(sub[sb], S);
-            if (sb + 1 < kCkpt / kSub && kSub * (sb + 1) < cnt) {
-#pragma unroll
-                for (int m = 0; m < kSub; ++m) rb.step(S, kSub * sb + m);
-            }
-        }
-    }
-    // Differentiate token tt (slot m of its sub-block) with S the state before it;
-    // the rows' column and scalar sums go to red[m], reds[m].
-    auto grad = [&](const Row& S, int tt, int m) {
-        Row kk, qq;
-        rb.lds_row(lds.k, tt, kk);
-        rb.lds_row(lds.q, tt, qq);
-        const int64_t gb = (t0 + tt) * in.num_v_heads + h;
-        const float alpha = lds.a[tt], b = lds.b[tt];
-        float w0 = 0.f, w1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            w0 = fmaf(S[0][e], kk[0][e], w0);
-            w1 = fmaf(S[1][e], kk[1][e], w1);
-        }
-        const float w = group_sum<L>(w0 + w1);
-        const float vm = lds.v[tt][rl];
-        const float u = b * (vm - alpha * w);
-        const float dom = lds.dout[tt][rl];
-        float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            dS[0][e] = fmaf(scale * dom, qq[0][e], dS[0][e]);
-            dS[1][e] = fmaf(scale * dom, qq[1][e], dS[1][e]);
-            d0 = fmaf(dS[0][e], kk[0][e], d0);
-            d1 = fmaf(dS[1][e], kk[1][e], d1);
-        }
-        const float du = group_sum<L>(d0 + d1);
-        float s_beta = 0.f, s_dw = 0.f, s_udo = 0.f, s_dss = 0.f;
-        if (c == 0) {
-            dv[gb * D + row] = b * du;
-            s_beta = du * (vm - alpha * w);
-            s_dw = du * w;
-            s_udo = u * dom;
-        }
-        const float ab = alpha * b;
-        Row colA, colB;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                colA[i][e] = S[i][e] * dom;
-                colB[i][e] = dS[i][e] * u - ab * S[i][e] * du;
-                s_dss = fmaf(dS[i][e], S[i][e], s_dss);
-                dS[i][e] = alpha * dS[i][e] - ab * du * kk[i][e];
-            }
-        // Sums over the row groups of the wave; the lanes with c == 0 hold the rows' scalar terms.
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                colA[i][e] = rows_sum<L, WL>(colA[i][e]);
-                colB[i][e] = rows_sum<L, WL>(colB[i][e]);
-            }
-        s_dss = group_sum<L>(s_dss);
-        s_beta = rows_sum<L, WL>(s_beta);
-        s_dw = rows_sum<L, WL>(s_dw);
-        s_udo = rows_sum<L, WL>(s_udo);
-        s_dss = rows_sum<L, WL>(s_dss);
-        if (ln < L) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                *reinterpret_cast<f32x4*>(&red[m][wv][0][rb.col(i, 0)]) =
-                    f32x4{colA[i][0], colA[i][1], colA[i][2], colA[i][3]};
-                *reinterpret_cast<f32x4*>(&red[m][wv][1][rb.col(i, 0)]) =
-                    f32x4{colB[i][0], colB[i][1], colB[i][2], colB[i][3]};
-            }
-        }
-        if (ln == 0) *reinterpret_cast<f32x4*>(&reds[m][wv][0]) = f32x4{s_beta, s_dw, s_udo, s_dss};
+    const int64_t off = (sl * hv + h) * (int64_t)D * D;
+    auto ld = [&](const void* p, int64_t idx) -> float {
+        if constexpr (BF16) return bf16_bits_to_float(reinterpret_cast<const uint16_t*>(p)[idx]);
+        else return reinterpret_cast<const float*>(p)[idx];
     };
-    // This block's parts of the sub-block's tokens tb .. tb + nt - 1 from the sums of
-    // the waves (linear in the sums, so the parts add up).
-    auto flush = [&](int tb, int nt) {
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+    // Stage K, Q (rows past cnt are zero), g and beta.
+    for (int e = tid; e < C * D; e += 256) {
+        const int t = e / D, c = e % D;
+        const int64_t idx = ((t0 + min(t, cnt - 1)) * hqk + hq) * D + c;
+        const float keep = t < cnt ? 1.f : 0.f;
+        Kf[t][c] = keep * ld(in.k, idx);
+        Qf[t][c] = keep * ld(in.q, idx);
+    }
+    if (tid < C) {
+        const int64_t gi = (t0 + min(tid, cnt - 1)) * hv + h;
+        const float keep = tid < cnt ? 1.f : 0.f;
+        gin[tid] = keep * in.g[gi];
+        bet[tid] = keep * in.beta[gi];
+    }
+    __syncthreads();
+    // Decays (wave 0) and the Gram matrices K K^T (wave 1), Q K^T (wave 2).
+    if (w == 0) {
+        if (ln < C) {
+            float s = 0.f, tot = 0.f;
+            for (int t = 0; t < C; ++t) {
+                tot += gin[t];
+                if (t == ln) s = tot;
+            }
+            gam[ln] = s;
+            Gam[ln] = exp_nonpos(s);
+            Gp[ln] = exp_nonpos(tot - s);
+        }
+    } else if (w <= 2) {
+        const float (*X)[KP] = w == 1 ? Kf : Qf;
+        f32x4 acc = zero4;
+        for (int kk = 0; kk < D / 4; ++kk) {
+            const int k = g4 * (D / 4) + kk;
+            acc = mfma4(X[m][k], Kf[m][k], acc);
+        }
+        float (*dst)[SP] = w == 1 ? KK : QK;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[4 * g4 + e][m] = acc[e];
+    }
+    __syncthreads();
+    // At, P and T = (I + diag(beta) At)^-1 (wave 0; lane c solves column c).
+    if (w == 0 && ln < C) {
+        const int c = ln;
+        for (int r = 0; r < C; ++r) {
+            const float dr = gam[r] - gam[c];
+            At[r][c] = c < r ? exp_nonpos(dr) * KK[r][c] : 0.f;
+            Pm[r][c] = c <= r ? exp_nonpos(dr) * QK[r][c] : 0.f;
+        }
+        float Tc[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            float s = r == c ? 1.f : 0.f;
+            const float br = bet[r];
+#pragma unroll
+            for (int p = 0; p < r; ++p) s = fmaf(-br * At[r][p], Tc[p], s);
+            Tc[r] = s;
+        }
+#pragma unroll
+        for (int r = 0; r < C; ++r) Tm[r][c] = Tc[r];
+    }
+    // Accumulators over the blocks: U G, dO S0, dU S0 for this wave's d tiles; dO U^T
+    // (wave 2) and dU U^T (wave 3); row sums for dbeta and du . AW; <G, S0>.
+    f32x4 accUG[TPW], accOS[TPW], accUS[TPW], accM = zero4;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) accUG[i] = accOS[i] = accUS[i] = zero4;
+    float p_db = 0.f, p_dw = 0.f, p_gs = 0.f;
+    const int vt = tid / 16, vp = tid % 16;   // token and column phase for the row sums
+
+    for (int rb = 0; rb < NB; ++rb) {
+        __syncthreads();   // the previous block's LDS reads are done (and T is written)
+        // Stage this block's rows of S0 and G, and its columns of V and dO.
+        {
+            const float* s0 = ck_s + off + (int64_t)rb * R * D;
+            const float* gg = ck_ds + off + (int64_t)rb * R * D;
+            for (int e = 4 * tid; e < R * D; e += 4 * 256) {
+                const int r = e / D, c = e % D;
+                *reinterpret_cast<f32x4*>(&Sb[r][c]) = *reinterpret_cast<const f32x4*>(s0 + e);
+                *reinterpret_cast<f32x4*>(&Gb[r][c]) = *reinterpret_cast<const f32x4*>(gg + e);
+            }
+            for (int e = tid; e < C * R; e += 256) {
+                const int t = e / R, c = e % R;
+                const int64_t idx = ((t0 + min(t, cnt - 1)) * hv + h) * D + rb * R + c;
+                const float keep = t < cnt ? 1.f : 0.f;
+                Vb[t][c] = keep * ld(in.v, idx);
+                dOb[t][c] = keep * ld(in.dout, idx);
+            }
+        }
         __syncthreads();
-        for (int x = tid; x < nt * 2 * D; x += NT) {
-            const int m = x / (2 * D), which = (x / D) % 2, jj = x % D;
-            const int tt = tb + m;
-            const int64_t pb = (((t0 + tt) * in.num_v_heads + h) * SPLIT + split) * D;
-            float a = 0.f;
+        // K S0^T and K G^T for the block's columns: 2 NTR tiles.
+        for (int tile = w; tile < 2 * NTR; tile += 4) {
+            const float (*B)[KP] = tile < NTR ? Sb : Gb;
+            const int nt = tile % NTR;
+            f32x4 acc = zero4;
+            for (int kk = 0; kk < D / 4; ++kk) {
+                const int k = g4 * (D / 4) + kk;
+                acc = mfma4(Kf[m][k], B[16 * nt + m][k], acc);
+            }
+            float (*dst)[BP] = tile < NTR ? KSs : KGs;
 #pragma unroll
-            for (int y = 0; y < NW; ++y) a += red[m][y][which][jj];
-            if (which == 0) {
-                float sudo = 0.f;
+            for (int e = 0; e < 4; ++e) dst[4 * g4 + e][16 * nt + m] = acc[e];
+        }
+        __syncthreads();
+        // U (waves 0 .. NTR - 1) and Z = P^T dO (waves 2 .. 2 + NTR - 1).
+        if (w < NTR) {
+            const int c = 16 * w + m;
+            f32x4 acc = zero4;
 #pragma unroll
-                for (int y = 0; y < NW; ++y) sudo += reds[m][y][2];
-                dq_p[pb + jj] = scale * fmaf(lds.a[tt], a, lds.k[tt][jj] * sudo);
-            } else {
-                dk_p[pb + jj] = a;
+            for (int kk = 0; kk < 4; ++kk) {
+                const int k = 4 * kk + g4;
+                acc = mfma4(Tm[m][k], bet[k] * (Vb[k][c] - Gam[k] * KSs[k][c]), acc);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Us[4 * g4 + e][c] = acc[e];
+        } else if (w >= 2 && w < 2 + NTR) {
+            const int c = 16 * (w - 2) + m;
+            f32x4 acc = zero4;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int k = 4 * kk + g4;
+                acc = mfma4(Pm[k][m], dOb[k][c], acc);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * g4 + e;
+                KGs[t][c] = fmaf(Gp[t], KGs[t][c], scale * acc[e]);   // Y = Gp K G^T + scale P^T dO
             }
         }
-        if (tid < nt) {
-            const int tt = tb + tid;
-            float sb = 0.f, sdw = 0.f, sdss = 0.f;
+        __syncthreads();
+        // AW = Gam K S0^T + At U, R = V - AW (waves 0 ..); dU = T^T Y (waves 2 ..).
+        if (w < NTR) {
+            const int c = 16 * w + m;
+            f32x4 acc = zero4;
 #pragma unroll
-            for (int y = 0; y < NW; ++y) {
-                sb += reds[tid][y][0];
-                sdw += reds[tid][y][1];
-                sdss += reds[tid][y][3];
+            for (int kk = 0; kk < 4; ++kk) {
+                const int k = 4 * kk + g4;
+                acc = mfma4(At[m][k], Us[k][c], acc);
             }
-            const int64_t gq = (((t0 + tt) * in.num_v_heads + h) * SPLIT + split) * 2;
-            gb_p[gq + 0] = lds.a[tt] * (sdss - lds.b[tt] * sdw);
-            gb_p[gq + 1] = sb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * g4 + e;
+                Rs[t][c] = Vb[t][c] - fmaf(Gam[t], KSs[t][c], acc[e]);
+            }
+        } else if (w >= 2 && w < 2 + NTR) {
+            const int c = 16 * (w - 2) + m;
+            f32x4 acc = zero4;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int k = 4 * kk + g4;
+                acc = mfma4(Tm[k][m], KGs[k][c], acc);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dUs[4 * g4 + e][c] = acc[e];
         }
-        __syncthreads();   // red and reds are free for the next sub-block
-    };
-    // Sub-blocks in reverse; inside each, its states in registers, then its tokens in reverse.
+        __syncthreads();
+        // dv, the row sums and <G, S0> on the block.
+        for (int c = vp; c < R; c += 16) {
+            const float du = dUs[vt][c], r = Rs[vt][c];
+            p_db = fmaf(du, r, p_db);
+            p_dw = fmaf(du, Vb[vt][c] - r, p_dw);
+            if (vt < cnt) dv[((t0 + vt) * hv + h) * D + rb * R + c] = bet[vt] * du;
+        }
+        for (int e = tid; e < R * D; e += 256) p_gs = fmaf(Gb[e / D][e % D], Sb[e / D][e % D], p_gs);
+        // U G, dO S0, dU S0 on this wave's d tiles (k: the block's rows).
 #pragma unroll
-    for (int sb = kCkpt / kSub - 1; sb >= 0; --sb) {
-        if (kSub * sb < cnt) {
-            Row st[kSub];
-            RB::copy(st[0], sub[sb]);
+        for (int i = 0; i < TPW; ++i) {
+            const int nt = w + 4 * i;
+            if (nt < NTD) {
 #pragma unroll
-            for (int m = 1; m < kSub; ++m) {
-                RB::copy(st[m], st[m - 1]);
-                if (kSub * sb + m < cnt) rb.step(st[m], kSub * sb + m - 1);
+                for (int kk = 0; kk < R / 4; ++kk) {
+                    const int k = 4 * kk + g4;
+                    const float sb = Sb[k][16 * nt + m];
+                    accUG[i] = mfma4(Us[m][k], Gb[k][16 * nt + m], accUG[i]);
+                    accOS[i] = mfma4(dOb[m][k], sb, accOS[i]);
+                    accUS[i] = mfma4(dUs[m][k], sb, accUS[i]);
+                }
+            }
+        }
+        if (w >= 2) {   // dO U^T (wave 2), dU U^T (wave 3)
+            const float (*X)[BP] = w == 2 ? dOb : dUs;
+#pragma unroll
+            for (int kk = 0; kk < R / 4; ++kk) {
+                const int k = 4 * kk + g4;
+                accM = mfma4(X[m][k], Us[m][k], accM);
+            }
+        }
+    }
+    // dO U^T and dU U^T to LDS; the row dots a, b, c of this wave's d tiles.
+    if (w >= 2) {
+        float (*dst)[SP] = w == 2 ? dOU : DUm;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[4 * g4 + e][m] = accM[e];
+    }
+    {
+        float pa[4] = {0.f, 0.f, 0.f, 0.f}, pbq[4] = {0.f, 0.f, 0.f, 0.f}, pc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int nt = w + 4 * i;
+            if (nt < NTD) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 4 * g4 + e, col = 16 * nt + m;
+                    pa[e] = fmaf(accUG[i][e], Kf[t][col], pa[e]);
+                    pbq[e] = fmaf(accOS[i][e], Qf[t][col], pbq[e]);
+                    pc[e] = fmaf(accUS[i][e], Kf[t][col], pc[e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pa[e] = group_sum<16>(pa[e]);
+            pbq[e] = group_sum<16>(pbq[e]);
+            pc[e] = group_sum<16>(pc[e]);
+        }
+        if (m == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                part[w][0][4 * g4 + e] = pa[e];
+                part[w][1][4 * g4 + e] = pbq[e];
+                part[w][2][4 * g4 + e] = pc[e];
+            }
+        }
+    }
+    // Row sums of dbeta and du . AW per token (16 lanes per token), <G, S0> over the block.
+    p_db = group_sum<16>(p_db);
+    p_dw = group_sum<16>(p_dw);
+    p_gs = group_sum<16>(p_gs);
+    p_gs = swap16_sum(p_gs);
+    p_gs = swap32_sum(p_gs);
+    if (ln == 0) red[w] = p_gs;
+    __syncthreads();
+    // M4 and M5 (wave 0, lane t builds row t); dg and dbeta (wave 1, lane t).
+    if (w == 0 && ln < C) {
+        const int t = ln;
+        const float bt = bet[t];
+        for (int s = 0; s < C; ++s) {
+            const float dts = gam[t] - gam[s];
+            M4[t][s] = s <= t ? exp_nonpos(dts) * dOU[t][s] : 0.f;
+            float m5 = 0.f;
+            if (s > t) m5 = exp_nonpos(-dts) * bet[s] * DUm[s][t];
+            if (s < t) m5 = bt * exp_nonpos(dts) * DUm[t][s];
+            M5[t][s] = m5;
+        }
+    }
+    if (w == 1 && ln < C) {
+        const int t = ln;
+        const float gs = red[0] + red[1] + red[2] + red[3];
+        float a_excl = 0.f, b_incl = 0.f, c_excl = 0.f, rect = 0.f;
+        for (int s = 0; s < C; ++s) {
+            const float a = Gp[s] * (part[0][0][s] + part[1][0][s] + part[2][0][s] + part[3][0][s]);
+            const float b = scale * Gam[s] * (part[0][1][s] + part[1][1][s] + part[2][1][s] + part[3][1][s]);
+            const float cc = Gam[s] * bet[s] * (part[0][2][s] + part[1][2][s] + part[2][2][s] + part[3][2][s]);
+            if (s < t) a_excl += a;
+            if (s >= t) b_incl += b;
+            if (s > t) c_excl += cc;
+            if (s >= t) {
+                for (int tau = 0; tau < t; ++tau) {
+                    float x = scale * Pm[s][tau] * dOU[s][tau];
+                    if (s > t) x -= bet[s] * At[s][tau] * DUm[s][tau];
+                    rect += x;
+                }
+            }
+        }
+        dgs[t] = exp_nonpos(gam[C - 1]) * gs + a_excl + b_incl - c_excl + rect;
+    }
+    __syncthreads();
+    // Each token's 16-lane group holds its dbeta and du . AW sums.
+    if (vp == 0 && vt < cnt) {
+        const int64_t gi = (t0 + vt) * hv + h;
+        dbeta[gi] = p_db;
+        dg[gi] = dgs[vt] - bet[vt] * p_dw;
+    }
+    // dQ and dK on this wave's d tiles.
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int nt = w + 4 * i;
+        if (nt < NTD) {
+            const int col = 16 * nt + m;
+            f32x4 q_, k_;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * g4 + e;
+                q_[e] = Gam[t] * accOS[i][e];
+                k_[e] = Gp[t] * accUG[i][e] - bet[t] * Gam[t] * accUS[i][e];
             }
 #pragma unroll
-            for (int m = kSub - 1; m >= 0; --m)
-                if (kSub * sb + m < cnt) grad(st[m], kSub * sb + m, m);
-            flush(kSub * sb, min(kSub, cnt - kSub * sb));
+            for (int kk = 0; kk < 4; ++kk) {
+                const int k = 4 * kk + g4;
+                q_ = mfma4(M4[m][k], Kf[k][col], q_);
+                k_ = mfma4(scale * M4[k][m], Qf[k][col], k_);
+                k_ = mfma4(-M5[m][k], Kf[k][col], k_);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * g4 + e;
+                if (t < cnt) {
+                    const int64_t gi = ((t0 + t) * hv + h) * D + col;
+                    dq_h[gi] = scale * q_[e];
+                    dk_h[gi] = k_[e];
+                }
+            }
         }
     }
 }
@@ -513,29 +717,11 @@ __global__ void backward_qk_sum_kernel(const float* __restrict__ part, float* __
     dst[e] = s;
 }
 
-// Pass 3, dg and dbeta: the sum of the row-block parts.
-__global__ void backward_gb_sum_kernel(const float* __restrict__ part, float* __restrict__ dg,
-                                       float* __restrict__ dbeta, int64_t n, int32_t split) {
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // over total_tokens * num_v_heads
-    if (e >= n) return;
-    float a = 0.f, b = 0.f;
-    for (int x = 0; x < split; ++x) {
-        a += part[(e * split + x) * 2 + 0];
-        b += part[(e * split + x) * 2 + 1];
-    }
-    dg[e] = a;
-    dbeta[e] = b;
-}
-
-static int bwd_split(int32_t d) { return d < 32 ? 1 : d / 32; }   // BwdShape<d>::SPLIT
-
 size_t backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_v_heads, int32_t d) {
     const int64_t slots = total_tokens / kCkpt + num_seqs;
-    const int split = bwd_split(d);
-    const size_t ck = (size_t)slots * num_v_heads * d * d * sizeof(float);
-    const size_t qk = (size_t)total_tokens * num_v_heads * split * d * sizeof(float);
-    const size_t gbp = (size_t)total_tokens * num_v_heads * split * 2 * sizeof(float);
-    return 2 * ck + 2 * qk + gbp;
+    const size_t ck = (size_t)slots * num_v_heads * d * d * sizeof(float);   // one checkpoint array
+    const size_t qk = (size_t)total_tokens * num_v_heads * d * sizeof(float);  // dq or dk per V head
+    return 2 * ck + 2 * qk;
 }
 
 template <int D, bool BF16>
@@ -545,12 +731,11 @@ static hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t stream) {
     float* ws = static_cast<float*>(a.workspace);
     const int64_t slots = a.total_tokens / kCkpt + a.num_seqs;
     const size_t ck = (size_t)slots * a.num_v_heads * D * D;
-    const size_t qk = (size_t)a.total_tokens * a.num_v_heads * Sh::SPLIT * D;
+    const size_t qk = (size_t)a.total_tokens * a.num_v_heads * D;
     float* ck_s = ws;
     float* ck_ds = ck_s + ck;
-    float* dq_p = ck_ds + ck;
-    float* dk_p = dq_p + qk;
-    float* gb_p = dk_p + qk;
+    float* dq_h = ck_ds + ck;
+    float* dk_h = dq_h + qk;
     const BwdIn in{a.q, a.k, a.v, a.d_out, a.g, a.beta, a.cu_seqlens, a.total_tokens,
                    a.num_seqs, a.num_qk_heads, a.num_v_heads, a.scale};
     const int64_t P = (int64_t)a.num_seqs * a.num_v_heads * Sh::SPLIT;
@@ -561,20 +746,17 @@ static hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.total_tokens == 0) return e;
     prof::begin(stream, "gdn_backward_grad");
-    hipLaunchKernelGGL((backward_grad_kernel<D, BF16>), dim3((unsigned)(slots * a.num_v_heads * Sh::SPLIT)),
-                       dim3(Sh::NT), 0, stream, in, ck_s, ck_ds, dq_p, dk_p, gb_p, a.dv);
+    hipLaunchKernelGGL((backward_grad_kernel<D, BF16>), dim3((unsigned)(slots * a.num_v_heads)), dim3(256), 0,
+                       stream, in, ck_s, ck_ds, dq_h, dk_h, a.dg, a.dbeta, a.dv);
     prof::end(stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nqk = a.total_tokens * a.num_qk_heads * D;
-    const int64_t nv = a.total_tokens * a.num_v_heads;
     const int group = a.num_v_heads / a.num_qk_heads;
     prof::begin(stream, "gdn_backward_sums");
-    hipLaunchKernelGGL(backward_qk_sum_kernel, dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0, stream, dq_p, a.dq,
-                       a.total_tokens, a.num_qk_heads, group, Sh::SPLIT, D);
-    hipLaunchKernelGGL(backward_qk_sum_kernel, dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0, stream, dk_p, a.dk,
-                       a.total_tokens, a.num_qk_heads, group, Sh::SPLIT, D);
-    hipLaunchKernelGGL(backward_gb_sum_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, stream, gb_p, a.dg,
-                       a.dbeta, nv, Sh::SPLIT);
+    hipLaunchKernelGGL(backward_qk_sum_kernel, dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0, stream, dq_h, a.dq,
+                       a.total_tokens, a.num_qk_heads, group, 1, D);
+    hipLaunchKernelGGL(backward_qk_sum_kernel, dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0, stream, dk_h, a.dk,
+                       a.total_tokens, a.num_qk_heads, group, 1, D);
     prof::end(stream);
     return hipGetLastError();
 }

@@ -223,11 +223,10 @@ def test_backward_rejects(lib, over, status):
 
 def test_backward_workspace_size(lib):
     ws = gdn.gdn_backward_workspace_size
-    # state and state-gradient checkpoints per 16 tokens (plus one per sequence), then q/k gradient
-    # parts per V head and per block of 32 state rows, then (dg, dbeta) parts per V head and row block
-    split = 128 // 32
+    # state and state-gradient checkpoints per 16 tokens (plus one per sequence), then dq and dk
+    # per V head (summed over the V heads of each QK head at the end)
     assert ws(4096, 1, 16, 32, 128, 128, gdn.GDN_BF16) == (2 * (4096 // 16 + 1) * 32 * 128 * 128 * 4
-                                                          + 2 * 4096 * 32 * split * 128 * 4 + 4096 * 32 * split * 2 * 4)
+                                                          + 2 * 4096 * 32 * 128 * 4)
     assert ws(100, 1, 3, 32, 128, 128, gdn.GDN_BF16) == 0
 
 
