@@ -1,61 +1,42 @@
-// Gradients of the Gated DeltaNet recurrence, token by token in fp32.
+// Gradients of the Gated DeltaNet recurrence in fp32, by chunks of 16 tokens.
 //
 // Forward rule per (sequence, V head), token t (alpha = exp(g), w = S k):
-//     u   = beta (v - alpha w)            S_t = alpha S + u k^T          o = scale S_t q
-// Reverse, with dS the gradient of S_t (it already holds every later token's
-// contribution) and S the state before token t:
-//     dS  += scale do q^T                 (the read-out)
-//     du   = dS k,   dv = beta du,   dbeta = du . (v - alpha w)
-//     dalpha = <dS, S> - beta du . w,    dg = alpha dalpha
-//     dk   = dS^T u - alpha beta S^T du,  dq = scale (alpha S^T do + k (u . do))
-//     dS  <- alpha dS - alpha beta du k^T (the gradient of the state before t)
-// Two facts shape the kernels. The update of dS does not involve S, so the
-// gradients at the interval boundaries follow from a reverse scan of their own.
-// And every row i of S and dS (value index i) evolves on its own: rows meet only
-// in the sums over i of dq, dk, dbeta and dalpha, which are linear in per-row
-// parts. The passes:
-//   1. scans, one workgroup per (sequence, V head, block of rows) and direction:
-//      forward, the state at the start of every interval of 16 tokens; reverse,
-//      the gradient of the state at the end of every interval (and of the
-//      initial state);
-//   2. one workgroup per (interval, V head, block of rows), all in parallel: the
-//      interval is cut into four sub-blocks of 4 tokens; a forward sweep keeps
-//      the state at each sub-block's start in registers, and each sub-block's
-//      states are rebuilt from there, again in registers, before its tokens are
-//      differentiated in reverse. The rows' parts of dq, dk, dg and dbeta go to
-//      the workspace, dv in full;
-//   3. the parts are added over row blocks (and, for dq and dk, over the V heads
-//      that share a QK head) in a fixed order, so results are deterministic.
-// Each row is held by d / 8 lanes, 8 key columns each, in registers; row sums
-// stay in the lane group (DPP), column sums go across row groups by shuffles
-// and across waves through LDS. An interval's inputs are staged in LDS once,
-// with the decays exp(g) taken there.
+//     u = beta (v - alpha w)        S_t = alpha S + u k^T        o = scale S_t q
+// Reverse, with E_t the gradient of S_t (every later token's contribution and
+// the read-out at t included) and S the state before token t:
+//     du = E_t k,  dv = beta du,  dbeta = du . (v - alpha w),  dg = alpha <E_t, S> - beta du . (alpha w)
+//     dk = E_t^T u - alpha beta S^T du,  dq = scale S_t^T do,
+//     E_{t-1} = alpha E_t - alpha beta du k^T + scale do_{t-1} q_{t-1}^T.
+// Over a chunk of 16 tokens (gamma the in-chunk cumulative sum of g, padded
+// tokens have g = 0, beta = 0 and zero inputs, so they are identity steps),
+// with At = exp(gamma_r - gamma_c) (k_r . k_c) strictly below the diagonal,
+// P = exp(gamma_r - gamma_c) (q_r . k_c) on and below it, T = (I + diag(beta)
+// At)^-1, Gam = exp(gamma), Gp = exp(gamma_last - gamma), S0 the state before
+// the chunk and G the gradient of the state after it, the chunk's writes and
+// their gradients are (rows are tokens):
+//     U  = T diag(beta) (V - diag(Gam) K S0^T)
+//     dU = T^T (diag(Gp) K G^T + scale P^T dO)
+//     S_after  = exp(gamma_last) S0 + (diag(Gp) U)^T K
+//     G_before = exp(gamma_last) G + (scale diag(Gam) dO)^T Q - (diag(Gam beta) dU)^T K
+// The passes:
+//   1. prep, every (chunk, V head) in parallel: gamma, beta, At, P and T;
+//   2. scans, per (sequence, V head, 16 state rows) and direction, chunk by
+//      chunk: S0 of every chunk (forward) and G of every chunk (reverse, and the
+//      gradient of the initial state);
+//   3. gradients, every (chunk, V head) in parallel, in closed form from S0 and G;
+//   4. dq and dk summed over the V heads of each QK head in a fixed order, so
+//      results are deterministic.
+// Every product is fp32 MFMA 16x16x4: lane (g, m) = (lane / 16, lane % 16) gives
+// A[m][k] and B[k][m] for the step's k and receives D[4 g + e][m], e = 0..3.
+// Steps take k = 4 kk + g, which spreads a row-major operand's reads over the
+// LDS banks; a contraction may also take its k in any other order that A and B share.
 #include "gdn_common.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr int kCkpt = 16;   // tokens per checkpoint interval
-constexpr int kSub = 4;     // tokens per sub-block of an interval
-
-template <int D>
-struct BwdShape {
-    static constexpr int L = D / 8;                  // lanes per state row (8 columns each)
-    static constexpr int ROWS = D < 32 ? D : 32;     // state rows per workgroup
-    static constexpr int SPLIT = D / ROWS;           // row blocks per (sequence, V head)
-    static constexpr int NT = ROWS * L;              // threads: one row per lane group
-    static constexpr int WL = NT < 64 ? NT : 64;     // lanes per wave in use
-    static constexpr int NW = (NT + 63) / 64;        // waves
-    static constexpr int KPT = kCkpt * D / NT;       // staged k (or q) elements per thread
-    static constexpr int VPT = (kCkpt * ROWS + NT - 1) / NT;   // staged v (or do) elements per thread
-};
-
-// Slot of interval j of sequence n among the checkpoints: cu[n] / 16 + n + j.
-// The ranges of different sequences are disjoint and below T / 16 + N.
-__device__ __forceinline__ int64_t ckpt_base(const int32_t* cu, int n) {
-    return cu ? (int64_t)(cu[n] / kCkpt) + n : 0;
-}
+constexpr int kC = 16;   // tokens per chunk; also the checkpoint interval
 
 struct BwdIn {
     const void *q, *k, *v, *dout;
@@ -66,7 +47,109 @@ struct BwdIn {
     float scale;
 };
 
-typedef float Row[2][4];   // a lane's 8 columns of one state row
+// Slot of chunk j of sequence n: cu[n] / 16 + n + j. The ranges of different
+// sequences are disjoint and below T / 16 + N.
+__device__ __forceinline__ int64_t ckpt_base(const int32_t* cu, int n) {
+    return cu ? (int64_t)(cu[n] / kC) + n : 0;
+}
+
+// The chunk that slot sl holds: its sequence, first token and token count;
+// false for a slot between two sequences' ranges.
+__device__ __forceinline__ bool slot_chunk(const BwdIn& in, int64_t sl, int& n, int64_t& t0, int& cnt) {
+    n = 0;
+    if (in.cu) {
+        int lo = 0, hi = in.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (ckpt_base(in.cu, mid) <= sl) lo = mid;
+            else hi = mid - 1;
+        }
+        n = lo;
+    }
+    const int64_t bos = in.cu ? (int64_t)in.cu[n] : 0, eos = in.cu ? (int64_t)in.cu[n + 1] : in.total_tokens;
+    const int64_t j = sl - ckpt_base(in.cu, n);
+    if (j < 0 || j >= (eos - bos + kC - 1) / kC) return false;
+    t0 = bos + j * kC;
+    cnt = (int)min((int64_t)kC, eos - t0);
+    return true;
+}
+
+template <bool BF16>
+__device__ __forceinline__ float ld_in(const void* p, int64_t idx) {
+    if constexpr (BF16) return bf16_bits_to_float(reinterpret_cast<const uint16_t*>(p)[idx]);
+    else return reinterpret_cast<const float*>(p)[idx];
+}
+
+// NE (1, 2, 4 or 8) consecutive elements at idx, aligned to their size, as fp32.
+template <bool BF16, int NE>
+__device__ __forceinline__ void ld_vec(const void* p, int64_t idx, float (&out)[NE]) {
+    static_assert(NE == 1 || NE == 2 || NE == 4 || NE == 8, "vector of 1, 2, 4 or 8");
+    if constexpr (BF16) {
+        const uint16_t* b = reinterpret_cast<const uint16_t*>(p) + idx;
+        if constexpr (NE == 1) {
+            out[0] = bf16_bits_to_float(*b);
+        } else {
+            typedef uint32_t u32v __attribute__((ext_vector_type(NE / 2)));
+            const u32v v = *reinterpret_cast<const u32v*>(b);
+#pragma unroll
+            for (int i = 0; i < NE / 2; ++i) {
+                out[2 * i] = __uint_as_float(v[i] << 16);
+                out[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+            }
+        }
+    } else {
+        const float* f = reinterpret_cast<const float*>(p) + idx;
+        if constexpr (NE == 1) {
+            out[0] = *f;
+        } else {
+            constexpr int V = NE < 4 ? NE : 4;
+            typedef float f32v __attribute__((ext_vector_type(V)));
+#pragma unroll
+            for (int h = 0; h < NE / V; ++h) {
+                const f32v v = *reinterpret_cast<const f32v*>(f + V * h);
+#pragma unroll
+                for (int i = 0; i < V; ++i) out[V * h + i] = v[i];
+            }
+        }
+    }
+}
+
+// The same elements as raw 32-bit words (bf16 pairs or fp32), for loads whose
+// values are not used until much later: converting them at once would make the
+// wave wait for the load right there.
+template <bool BF16, int NE>
+struct Raw {
+    static constexpr int W = BF16 ? (NE + 1) / 2 : NE;
+    uint32_t w[W];
+};
+template <bool BF16, int NE>
+__device__ __forceinline__ void ld_raw(const void* p, int64_t idx, Raw<BF16, NE>& r) {
+    static_assert(NE == 1 || NE == 2 || NE == 4 || NE == 8, "vector of 1, 2, 4 or 8");
+    if constexpr (BF16 && NE == 1) {
+        r.w[0] = reinterpret_cast<const uint16_t*>(p)[idx];
+    } else {
+        const uint32_t* base = BF16 ? reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(p) + idx)
+                                    : reinterpret_cast<const uint32_t*>(reinterpret_cast<const float*>(p) + idx);
+        constexpr int W = Raw<BF16, NE>::W, V = W < 4 ? W : 4;
+        typedef uint32_t u32v __attribute__((ext_vector_type(V)));
+#pragma unroll
+        for (int h = 0; h < W / V; ++h) {
+            const u32v v = *reinterpret_cast<const u32v*>(base + V * h);
+#pragma unroll
+            for (int i = 0; i < V; ++i) r.w[V * h + i] = v[i];
+        }
+    }
+}
+template <bool BF16, int NE>
+__device__ __forceinline__ float raw_at(const Raw<BF16, NE>& r, int i) {
+    if constexpr (!BF16) return __uint_as_float(r.w[i]);
+    else if constexpr (NE == 1) return __uint_as_float(r.w[0] << 16);
+    else return __uint_as_float((i & 1) ? (r.w[i / 2] & 0xFFFF0000u) : (r.w[i / 2] << 16));
+}
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 // x[lane] + x[lane ^ 16] and x[lane] + x[lane ^ 32]: each swap instruction
 // exchanges half of one register with half of the other, so with both operands
@@ -79,269 +162,359 @@ __device__ __forceinline__ float swap32_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-// Sum over the lanes of a wave's first WL lanes that share lane % L.
-template <int L, int WL>
-__device__ __forceinline__ float rows_sum(float x) {
-#pragma unroll
-    for (int mask = L; mask < WL; mask *= 2) {
-        if (mask == 16) x = swap16_sum(x);
-        else if (mask == 32) x = swap32_sum(x);
-        else x += __shfl_xor(x, mask);
-    }
-    return x;
+
+// LDS written by some lanes of a wave and then read by others of the same wave.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Per-workgroup view: a row block of one (sequence, V head), its interval staging
-// in LDS and the per-row arithmetic shared by the passes.
-template <int D, bool BF16>
-struct RowBlock {
-    using Sh = BwdShape<D>;
-    static constexpr int L = Sh::L, ROWS = Sh::ROWS, NT = Sh::NT, KPT = Sh::KPT, VPT = Sh::VPT;
-    struct alignas(16) Lds {
-        float k[kCkpt][D], q[kCkpt][D];
-        float v[kCkpt][ROWS], dout[kCkpt][ROWS];   // this block's rows only
-        float a[kCkpt], b[kCkpt];                  // exp(g), beta
-    };
-    // One interval's inputs on their way from HBM to LDS.
-    struct Fetch {
-        float k[KPT], q[KPT], v[VPT], dout[VPT], g, b;
-    };
-    const BwdIn& in;
-    Lds& s;
-    int tid, c, rl, row, h, hq, split;
-
-    __device__ RowBlock(const BwdIn& in_, Lds& s_, int h_, int split_) : in(in_), s(s_), h(h_), split(split_) {
-        tid = threadIdx.x;
-        c = tid % L;
-        rl = tid / L;
-        row = split * ROWS + rl;
-        hq = h / (in.num_v_heads / in.num_qk_heads);
-    }
-    __device__ __forceinline__ int col(int i, int e) const { return 4 * (c + L * i) + e; }
-    __device__ __forceinline__ float ld(const void* p, int64_t idx) const {
-        if constexpr (BF16) return bf16_bits_to_float(reinterpret_cast<const uint16_t*>(p)[idx]);
-        else return reinterpret_cast<const float*>(p)[idx];
-    }
-    // Global loads of tokens t0 .. t1 - 1 (1 to 16 of them) into registers. Slots
-    // past t1 load token t1 - 1 again (no branch around the loads); they are
-    // never read.
-    __device__ __forceinline__ void fetch(Fetch& f, int64_t t0, int64_t t1, bool want_q, bool want_v,
-                                          bool want_do) const {
-        const int last = (int)(t1 - t0) - 1;
-        const int hqk = in.num_qk_heads, hv = in.num_v_heads;
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            const int e = tid + r * NT, tt = min(e / D, last), jj = e % D;
-            const int64_t idx = ((t0 + tt) * hqk + hq) * D + jj;
-            f.k[r] = ld(in.k, idx);
-            if (want_q) f.q[r] = ld(in.q, idx);
-        }
-#pragma unroll
-        for (int r = 0; r < VPT; ++r) {
-            const int e = min(tid + r * NT, kCkpt * ROWS - 1), tt = min(e / ROWS, last), rr = e % ROWS;
-            const int64_t idx = ((t0 + tt) * hv + h) * D + split * ROWS + rr;
-            if (want_v) f.v[r] = ld(in.v, idx);
-            if (want_do) f.dout[r] = ld(in.dout, idx);
-        }
-        const int64_t gi = (t0 + min(tid, last)) * hv + h;
-        f.g = in.g[gi];
-        f.b = in.beta[gi];
-    }
-    // Fetched registers into LDS, after every thread has finished with the
-    // previous contents.
-    __device__ __forceinline__ void commit(const Fetch& f, bool want_q, bool want_v, bool want_do) {
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            const int e = tid + r * NT;
-            s.k[e / D][e % D] = f.k[r];
-            if (want_q) s.q[e / D][e % D] = f.q[r];
-        }
-#pragma unroll
-        for (int r = 0; r < VPT; ++r) {
-            const int e = tid + r * NT;
-            if (e < kCkpt * ROWS) {
-                if (want_v) s.v[e / ROWS][e % ROWS] = f.v[r];
-                if (want_do) s.dout[e / ROWS][e % ROWS] = f.dout[r];
-            }
-        }
-        if (tid < kCkpt) {
-            s.a[tid] = exp_nonpos(f.g);
-            s.b[tid] = f.b;
-        }
-        __syncthreads();
-    }
-    __device__ __forceinline__ void lds_row(const float (*X)[D], int tt, Row& x) const {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const f32x4 y = *reinterpret_cast<const f32x4*>(&X[tt][col(i, 0)]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[i][e] = y[e];
-        }
-    }
-    __device__ __forceinline__ void load_row(const float* src, Row& x) const {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const f32x4 y = src ? *reinterpret_cast<const f32x4*>(src + row * D + col(i, 0)) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[i][e] = y[e];
-        }
-    }
-    __device__ __forceinline__ void store_row(float* dst, const Row& x) const {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            *reinterpret_cast<f32x4*>(dst + row * D + col(i, 0)) = f32x4{x[i][0], x[i][1], x[i][2], x[i][3]};
-    }
-    __device__ __forceinline__ static void copy(Row& d, const Row& x) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) d[i][e] = x[i][e];
-    }
-    // One forward step of this row of S for staged token tt.
-    __device__ __forceinline__ void step(Row& S, int tt) const {
-        Row kk;
-        lds_row(s.k, tt, kk);
-        const float alpha = s.a[tt], b = s.b[tt];
-        float w0 = 0.f, w1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            w0 = fmaf(S[0][e], kk[0][e], w0);
-            w1 = fmaf(S[1][e], kk[1][e], w1);
-        }
-        const float w = group_sum<L>(w0 + w1);
-        const float u = b * (s.v[tt][rl] - alpha * w);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) S[i][e] = fmaf(alpha, S[i][e], u * kk[i][e]);
-    }
-    // One reverse step of this row of dS for staged token tt (read-out, then the
-    // gradient of the state before the token).
-    __device__ __forceinline__ void rstep(Row& dS, int tt) const {
-        Row kk, qq;
-        lds_row(s.k, tt, kk);
-        lds_row(s.q, tt, qq);
-        const float alpha = s.a[tt], b = s.b[tt];
-        const float sd = in.scale * s.dout[tt][rl];
-        float d0 = 0.f, d1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            dS[0][e] = fmaf(sd, qq[0][e], dS[0][e]);
-            dS[1][e] = fmaf(sd, qq[1][e], dS[1][e]);
-            d0 = fmaf(dS[0][e], kk[0][e], d0);
-            d1 = fmaf(dS[1][e], kk[1][e], d1);
-        }
-        const float du = group_sum<L>(d0 + d1);
-        const float ab = alpha * b;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dS[i][e] = alpha * dS[i][e] - ab * du * kk[i][e];
-    }
+// Per (chunk slot, V head): the chunk's factors.
+struct alignas(16) ChunkFac {
+    float gam[kC], bet[kC];   // in-chunk cumulative g; beta (0 past the chunk's tokens)
+    float Gam[kC], Gp[kC];    // exp(gamma), exp(gamma_last - gamma)
+    float T[kC][kC];          // (I + diag(beta) At)^-1
+    float P[kC][kC];          // exp(gamma_r - gamma_c) (q_r . k_c), c <= r
+    float At[kC][kC];         // exp(gamma_r - gamma_c) (k_r . k_c), c < r
 };
 
-// Pass 1: blocks [0, P) scan forward and store the state rows at the start of each
-// interval; blocks [P, 2P) scan in reverse and store the gradient rows at the end
-// of each interval, then the gradient of the initial state. P = N * Hv * SPLIT.
-// The next interval's inputs are fetched while the current one is processed.
+// Pass 1: one wave per (slot, V head).
 template <int D, bool BF16>
-__global__ __launch_bounds__(BwdShape<D>::NT) void backward_scan_kernel(
-    BwdIn in, const float* __restrict__ initial_state, const float* __restrict__ dfinal,
-    float* __restrict__ dinit, float* __restrict__ ck_s, float* __restrict__ ck_ds) {
-    using Sh = BwdShape<D>;
-    using RB = RowBlock<D, BF16>;
-    __shared__ typename RB::Lds lds;
-    const int64_t P = (int64_t)in.num_seqs * in.num_v_heads * Sh::SPLIT;
-    const bool rev = blockIdx.x >= P;
-    const int64_t b = rev ? blockIdx.x - P : blockIdx.x;
-    const int split = (int)(b % Sh::SPLIT);
-    const int nh = (int)(b / Sh::SPLIT);
-    const int n = nh / in.num_v_heads, h = nh % in.num_v_heads;
-    RB rb(in, lds, h, split);
-    const int64_t bos = in.cu ? (int64_t)in.cu[n] : 0, eos = in.cu ? (int64_t)in.cu[n + 1] : in.total_tokens;
-    const int64_t sbase = ((int64_t)n * in.num_v_heads + h) * D * D;
-    const int64_t cbase = ckpt_base(in.cu, n);
-    const int64_t nint = (eos - bos + kCkpt - 1) / kCkpt;
-    auto slot = [&](float* base, int64_t j) { return base + ((cbase + j) * in.num_v_heads + h) * (int64_t)D * D; };
-    auto span = [&](int64_t j, int64_t& t0, int64_t& t1) {
-        t0 = bos + j * kCkpt;
-        t1 = (t0 + kCkpt < eos) ? t0 + kCkpt : eos;
-    };
-    Row X;
-    typename RB::Fetch f;
-    int64_t t0, t1;
-    if (!rev) {
-        rb.load_row(initial_state ? initial_state + sbase : nullptr, X);
-        if (nint > 0) {
-            span(0, t0, t1);
-            rb.fetch(f, t0, t1, false, true, false);
-        }
-        for (int64_t j = 0; j < nint; ++j) {
-            rb.store_row(slot(ck_s, j), X);
-            span(j, t0, t1);
-            rb.commit(f, false, true, false);
-            if (j + 1 < nint) {
-                int64_t u0, u1;
-                span(j + 1, u0, u1);
-                rb.fetch(f, u0, u1, false, true, false);
-            }
-            const int cnt = (int)(t1 - t0);
-            if (cnt == kCkpt) {
+__global__ __launch_bounds__(64) void backward_prep_kernel(BwdIn in, ChunkFac* __restrict__ fac) {
+    constexpr int KP = D + 4;
+    __shared__ __align__(16) float Kf[kC][KP], Qf[kC][KP];
+    __shared__ float gin[kC], bet[kC], gam[kC], At[kC][kC + 1];
+    const int hv = in.num_v_heads, h = blockIdx.x % hv, hq = h / (hv / in.num_qk_heads);
+    const int64_t sl = blockIdx.x / hv;
+    int n, cnt;
+    int64_t t0;
+    if (!slot_chunk(in, sl, n, t0, cnt)) return;
+    const int ln = threadIdx.x, g4 = ln / 16, m = ln % 16;
+    for (int e = ln; e < kC * D; e += 64) {
+        const int t = e / D, c = e % D;
+        const int64_t idx = ((t0 + min(t, cnt - 1)) * in.num_qk_heads + hq) * D + c;
+        const float keep = t < cnt ? 1.f : 0.f;
+        Kf[t][c] = keep * ld_in<BF16>(in.k, idx);
+        Qf[t][c] = keep * ld_in<BF16>(in.q, idx);
+    }
+    if (ln < kC) {
+        const int64_t gi = (t0 + min(ln, cnt - 1)) * hv + h;
+        const float keep = ln < cnt ? 1.f : 0.f;
+        gin[ln] = keep * in.g[gi];
+        bet[ln] = keep * in.beta[gi];
+    }
+    __syncthreads();
+    if (ln < kC) {
+        float s = 0.f;
+        for (int t = 0; t <= ln; ++t) s += gin[t];
+        gam[ln] = s;
+    }
+    f32x4 kk_ = {0.f, 0.f, 0.f, 0.f}, qk_ = kk_;
+    for (int kk = 0; kk < D / 4; ++kk) {
+        const int k = 4 * kk + g4;
+        const float kv = Kf[m][k];
+        kk_ = mfma4(kv, kv, kk_);
+        qk_ = mfma4(Qf[m][k], kv, qk_);
+    }
+    __syncthreads();
+    ChunkFac& F = fac[sl * hv + h];
 #pragma unroll
-                for (int tt = 0; tt < kCkpt; ++tt) rb.step(X, tt);
-            } else {
-                for (int tt = 0; tt < cnt; ++tt) rb.step(X, tt);
-            }
-        }
-    } else {
-        rb.load_row(dfinal ? dfinal + sbase : nullptr, X);
-        if (nint > 0) {
-            span(nint - 1, t0, t1);
-            rb.fetch(f, t0, t1, true, false, true);
-        }
-        for (int64_t j = nint - 1; j >= 0; --j) {
-            rb.store_row(slot(ck_ds, j), X);
-            span(j, t0, t1);
-            rb.commit(f, true, false, true);
-            if (j > 0) {
-                int64_t u0, u1;
-                span(j - 1, u0, u1);
-                rb.fetch(f, u0, u1, true, false, true);
-            }
-            const int cnt = (int)(t1 - t0);
-            if (cnt == kCkpt) {
+    for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g4 + e, c = m;
+        const float dec = exp_nonpos(fminf(gam[r] - gam[c], 0.f));
+        const float at = c < r ? dec * kk_[e] : 0.f;
+        At[r][c] = at;
+        F.At[r][c] = at;
+        F.P[r][c] = c <= r ? dec * qk_[e] : 0.f;
+    }
+    if (ln < kC) {
+        F.gam[ln] = gam[ln];
+        F.bet[ln] = bet[ln];
+        F.Gam[ln] = exp_nonpos(gam[ln]);
+        F.Gp[ln] = exp_nonpos(gam[kC - 1] - gam[ln]);
+    }
+    __syncthreads();
+    // T by forward substitution, lane c solving column c.
+    if (ln < kC) {
+        const int c = ln;
+        float Tc[kC];
 #pragma unroll
-                for (int tt = kCkpt - 1; tt >= 0; --tt) rb.rstep(X, tt);
-            } else {
-                for (int tt = cnt - 1; tt >= 0; --tt) rb.rstep(X, tt);
-            }
+        for (int r = 0; r < kC; ++r) {
+            float s = r == c ? 1.f : 0.f;
+            const float br = bet[r];
+#pragma unroll
+            for (int p = 0; p < r; ++p) s = fmaf(-br * At[r][p], Tc[p], s);
+            Tc[r] = s;
         }
-        if (dinit) rb.store_row(dinit + sbase, X);
+#pragma unroll
+        for (int r = 0; r < kC; ++r) F.T[r][c] = Tc[r];
     }
 }
 
-// Pass 2, one workgroup (4 waves) per (interval, V head): the interval as a
-// chunk of 16 tokens (padded with g = 0, beta = 0 and zero inputs, which are
-// identity steps), entry state S0 and end gradient G from the scans. With
-// gamma the in-chunk cumulative sum of g, Gam = exp(gamma), Gp = exp(gamma_last
-// - gamma), dec[r][c] = exp(gamma_r - gamma_c), At = dec (K K^T) strictly below
-// the diagonal, A = diag(beta) At, P = dec (Q K^T) on and below it and
-// T = (I + A)^-1, the token rule unrolls to (rows are tokens):
-//   U  = T diag(beta) (V - diag(Gam) K S0^T)       AW = diag(Gam) K S0^T + At U
-//   dU = T^T (diag(Gp) K G^T + scale P^T dO)       (du_t = E_t k_t, E_t the state gradient)
+// Pass 2: blocks [0, P) scan forward, blocks [P, 2P) in reverse, P = N Hv (d / 16);
+// a block holds 16 state rows (value tile vt) of one (sequence, V head) as
+// transposed 16 x 16 tiles in its waves' MFMA accumulators, wave w the key tiles
+// w, w + 4, ... (lane (g, m) of key tile tk: rows 16 vt + m, columns 16 tk + 4 g + e).
+// That layout is also the B operand of K S0^T when step (tk, e) takes, in lane
+// group g, key 16 tk + 4 g + e, so the state never leaves the registers; each
+// wave adds its key tiles' share of K S0^T (or K G^T) and the shares meet in LDS,
+// one barrier per chunk. The inputs of the next chunks are loaded into
+// registers one chunk ahead and kept in a ring of three LDS buffers.
+template <int D>
+struct ScanShape {
+    static constexpr int NTD = D / 16;            // 16-wide tiles over d
+    static constexpr int TPW = (NTD + 3) / 4;     // key tiles per wave
+    static constexpr int EPT = D / 16;            // staged k (or q) elements per thread: one row piece
+};
+
+template <int D>
+struct ScanSmem {
+    static constexpr int KP = D + 1, SP = kC + 1;   // odd pitches spread a column over the banks
+    float Kc[3][kC][KP], Qc[3][kC][KP];
+    float Xc[3][kC][SP], Tc[3][kC][SP], Pc[3][kC][SP], Gc[3][kC], Hc[3][kC], bc[3][kC];   // Hc: Gp
+    float part[2][4][kC][SP], Uw[4][kC][SP];
+};
+
+// One direction's scan (REV: the gradient, in reverse); b indexes (sequence, V head, value tile).
+template <int D, bool BF16, bool REV>
+__device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, const ChunkFac* __restrict__ fac,
+                                          const float* __restrict__ init, float* __restrict__ dinit,
+                                          float* __restrict__ ck, int64_t b) {
+    using Sh = ScanShape<D>;
+    constexpr int NTD = Sh::NTD, TPW = Sh::TPW, EPT = Sh::EPT;
+    constexpr bool rev = REV;
+    auto& Kc = sm.Kc;
+    auto& Qc = sm.Qc;
+    auto& Xc = sm.Xc;
+    auto& Tc = sm.Tc;
+    auto& Pc = sm.Pc;
+    auto& Gc = sm.Gc;
+    auto& Hc = sm.Hc;
+    auto& bc = sm.bc;
+    auto& part = sm.part;
+    auto& Uw = sm.Uw;
+    const int hv = in.num_v_heads, hqk = in.num_qk_heads;
+    const int vt = (int)(b % NTD);
+    const int nh = (int)(b / NTD);
+    const int n = nh / hv, h = nh % hv, hq = h / (hv / hqk);
+    const int64_t bos = in.cu ? (int64_t)in.cu[n] : 0, eos = in.cu ? (int64_t)in.cu[n + 1] : in.total_tokens;
+    const int64_t cbase = ckpt_base(in.cu, n);
+    const int nint = (int)((eos - bos + kC - 1) / kC);
+    const int tid = threadIdx.x, w = tid / 64, ln = tid % 64, g4 = ln / 16, m = ln % 16;
+    const int64_t sbase = ((int64_t)n * hv + h) * D * D;
+    const float scale = in.scale;
+    const int row = 16 * vt + m;   // this lane's state row
+
+    // One chunk's inputs in registers. Thread tid stages token row tid / 16 of K
+    // (and Q), columns EPT (tid % 16) .. + EPT - 1, and element (tid / 16, tid % 16)
+    // of the 16 x 16 value tile and of T, P.
+    struct Pre {
+        Raw<BF16, EPT> k, q;
+        Raw<BF16, 1> x;
+        float t, p, G, H, b;
+        bool keep;   // the thread's token row is inside the chunk (applied at commit, so
+                     // that nothing waits for the loads before then)
+    };
+    const int ktt = tid / 16, kcol = EPT * (tid % 16);
+    auto chunk_at = [&](int q) { return rev ? nint - 1 - q : q; };   // q-th chunk in scan order
+    auto fetch = [&](Pre& pre, int q) {
+        const int c = chunk_at(q);
+        const int64_t t0 = bos + (int64_t)c * kC;
+        const int cnt = (int)min((int64_t)kC, eos - t0);
+        const int rr = min(ktt, cnt - 1);   // rows past the chunk re-read its last row, then read as 0
+        pre.keep = ktt < cnt;
+        const int64_t kb = (t0 * hqk + hq) * D + (int64_t)rr * hqk * D + kcol;
+        ld_raw<BF16, EPT>(in.k, kb, pre.k);
+        if constexpr (REV) ld_raw<BF16, EPT>(in.q, kb, pre.q);
+        const int64_t xb = (t0 * hv + h) * D + (int64_t)rr * hv * D + 16 * vt + tid % 16;
+        ld_raw<BF16, 1>(REV ? in.dout : in.v, xb, pre.x);
+        const ChunkFac& F = fac[(cbase + c) * hv + h];
+        pre.t = F.T[tid / 16][tid % 16];
+        if constexpr (REV) pre.p = F.P[tid / 16][tid % 16];
+        pre.G = F.Gam[tid % kC];   // every lane loads (no branch around the loads); tid < 16 keep theirs
+        pre.H = F.Gp[tid % kC];
+        pre.b = F.bet[tid % kC];
+    };
+    auto commit = [&](const Pre& pre, int buf) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            Kc[buf][ktt][kcol + i] = pre.keep ? raw_at(pre.k, i) : 0.f;
+            if constexpr (REV) Qc[buf][ktt][kcol + i] = pre.keep ? raw_at(pre.q, i) : 0.f;
+        }
+        Xc[buf][tid / 16][tid % 16] = pre.keep ? raw_at(pre.x, 0) : 0.f;
+        Tc[buf][tid / 16][tid % 16] = pre.t;
+        if constexpr (REV) Pc[buf][tid / 16][tid % 16] = pre.p;
+        if (tid < kC) {
+            Gc[buf][tid] = pre.G;
+            Hc[buf][tid] = pre.H;
+            bc[buf][tid] = pre.b;
+        }
+    };
+
+    // The state (forward) or its gradient (reverse), transposed tiles.
+    f32x4 acc[TPW];
+    {
+        const float* src = init ? init + sbase : nullptr;
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int tk = w + 4 * i;
+            acc[i] = (src && tk < NTD) ? *reinterpret_cast<const f32x4*>(src + row * D + 16 * tk + 4 * g4)
+                                       : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    // Chunks q and q + 1 sit in LDS when chunk q starts; two register sets hold
+    // chunks q + 2 and q + 3 on their way (loaded two chunks ahead of use).
+    Pre pa, pb;
+    if (nint > 0) {
+        fetch(pa, 0);
+        commit(pa, 0);
+    }
+    if (nint > 1) {
+        fetch(pb, 1);
+        commit(pb, 1);
+    }
+    __syncthreads();
+    if (nint > 2) fetch(pa, 2);
+    if (nint > 3) fetch(pb, 3);
+    auto chunk = [&](int q, Pre& pre) {
+        const int c = chunk_at(q), bb = q % 3, pp = q & 1;
+        // Checkpoint: the state at the chunk's start (forward), the gradient at its end (reverse).
+        float* dst = ck + ((cbase + c) * hv + h) * (int64_t)D * D + row * D;
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int tk = w + 4 * i;
+            if (tk < NTD) *reinterpret_cast<f32x4*>(dst + 16 * tk + 4 * g4) = acc[i];
+        }
+        // This wave's share of K X^T (X: the state or its gradient).
+        {
+            f32x4 ps = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int tk = w + 4 * i;
+                if (tk < NTD) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ps = mfma4(Kc[bb][m][16 * tk + 4 * g4 + e], acc[i][e], ps);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[pp][w][4 * g4 + e][m] = ps[e];
+        }
+        // Reverse: Z = P^T dO (no dependence on the gradient).
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (REV) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) z = mfma4(Pc[bb][4 * kk + g4][m], Xc[bb][4 * kk + g4][m], z);
+        }
+        __syncthreads();
+        // Buffer (q + 2) % 3 was last read in chunk q - 1, which every wave has finished.
+        if (q + 2 < nint) commit(pre, (q + 2) % 3);
+        if (q + 4 < nint) fetch(pre, q + 4);
+        const float GL = Gc[bb][kC - 1];   // exp(gamma_last)
+        if constexpr (!REV) {
+            // U = T diag(beta) (V - diag(Gam) K S0^T), then Gp U to this wave's LDS rows.
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int tau = 4 * kk + g4;
+                const float ks = part[pp][0][tau][m] + part[pp][1][tau][m] + part[pp][2][tau][m] + part[pp][3][tau][m];
+                const float xv = bc[bb][tau] * (Xc[bb][tau][m] - Gc[bb][tau] * ks);
+                u = mfma4(Tc[bb][m][tau], xv, u);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tau = 4 * g4 + e;
+                Uw[w][tau][m] = Hc[bb][tau] * u[e];
+            }
+            wave_lds_sync();
+            // S^T <- exp(gamma_last) S^T + K^T (Gp U)
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int tk = w + 4 * i;
+                if (tk < NTD) {
+                    f32x4 a = acc[i] * GL;
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const int tau = 4 * kk + g4;
+                        a = mfma4(Kc[bb][tau][16 * tk + m], Uw[w][tau][m], a);
+                    }
+                    acc[i] = a;
+                }
+            }
+        } else {
+            // Y = Gp K G^T + scale Z, dU = T^T Y, then -Gam beta dU to this wave's LDS rows.
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tau = 4 * g4 + e;
+                const float kg = part[pp][0][tau][m] + part[pp][1][tau][m] + part[pp][2][tau][m] + part[pp][3][tau][m];
+                Uw[w][tau][m] = fmaf(Hc[bb][tau], kg, scale * z[e]);
+            }
+            wave_lds_sync();
+            f32x4 du = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) du = mfma4(Tc[bb][4 * kk + g4][m], Uw[w][4 * kk + g4][m], du);
+            wave_lds_sync();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tau = 4 * g4 + e;
+                Uw[w][tau][m] = -Gc[bb][tau] * bc[bb][tau] * du[e];
+            }
+            wave_lds_sync();
+            // G^T <- exp(gamma_last) G^T + Q^T (scale Gam dO) + K^T (-Gam beta dU)
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int tk = w + 4 * i;
+                if (tk < NTD) {
+                    f32x4 a = acc[i] * GL;
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const int tau = 4 * kk + g4;
+                        a = mfma4(Qc[bb][tau][16 * tk + m], scale * Gc[bb][tau] * Xc[bb][tau][m], a);
+                        a = mfma4(Kc[bb][tau][16 * tk + m], Uw[w][tau][m], a);
+                    }
+                    acc[i] = a;
+                }
+            }
+        }
+    };
+    for (int q = 0; q < nint; q += 2) {
+        chunk(q, pa);
+        if (q + 1 < nint) chunk(q + 1, pb);
+    }
+    if (REV && dinit) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int tk = w + 4 * i;
+            if (tk < NTD) *reinterpret_cast<f32x4*>(dinit + sbase + row * D + 16 * tk + 4 * g4) = acc[i];
+        }
+    }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void backward_scan_kernel(
+    BwdIn in, const ChunkFac* __restrict__ fac, const float* __restrict__ initial_state,
+    const float* __restrict__ dfinal, float* __restrict__ dinit, float* __restrict__ ck_s,
+    float* __restrict__ ck_ds) {
+    __shared__ __align__(16) ScanSmem<D> sm;
+    const int64_t P = (int64_t)in.num_seqs * in.num_v_heads * (D / 16);
+    if (blockIdx.x >= P) scan_body<D, BF16, true>(sm, in, fac, dfinal, dinit, ck_ds, blockIdx.x - P);
+    else scan_body<D, BF16, false>(sm, in, fac, initial_state, nullptr, ck_s, blockIdx.x);
+}
+
+// Pass 3, one workgroup (4 waves) per (chunk slot, V head), from the chunk's
+// factors, S0 and G. With U, dU as above, AW = diag(Gam) K S0^T + At U (alpha w
+// of every token) and the rows' dot products over the value index:
 //   dv = diag(beta) dU,   dbeta_t = du_t . (v_t - AW_t)
 //   dQ = scale (diag(Gam) dO S0 + M4 K),           M4 = [tau <= t] dec (dO U^T)
 //   dK = diag(Gp) U G - diag(beta Gam) dU S0 + scale M4^T Q - M5 K,
 //        M5[t][s] = [s > t] dec[s][t] beta_s (dU U^T)[s][t] + [s < t] beta_t dec[t][s] (dU U^T)[t][s]
 //   dg_t = exp(gamma_last) <G, S0> + sum_{tau < t} a_tau + sum_{s >= t} b_s - sum_{s > t} c_s
 //          + sum_{s >= t, tau < t} scale P[s][tau] (dO U^T)[s][tau]
-//          - sum_{s > t, tau < t} A[s][tau] (dU U^T)[s][tau] - beta_t du_t . AW_t,
-//   a = Gp (U G . K), b = scale Gam (dO S0 . Q), c = Gam beta (dU S0 . K) (row dots).
-// Products over the value index (U G, dO S0, dU S0, dO U^T, dU U^T, <G, S0>) run
-// over blocks of 32 state rows staged in LDS and accumulate in registers. All
-// products are fp32 MFMA 16x16x4 (lane (g, m): A[m][k], B[k][m], D[4 g + e][m];
-// any fixed order of k serves, so long contractions take k = g (K / 4) + kk).
+//          - sum_{s > t, tau < t} beta_s At[s][tau] (dU U^T)[s][tau] - beta_t du_t . AW_t,
+//   a = Gp (U G . K), b = scale Gam (dO S0 . Q), c = Gam beta (dU S0 . K) (row dots),
+// dec[r][c] = exp(gamma_r - gamma_c). Products over the value index (U G, dO S0,
+// dU S0, dO U^T, dU U^T, <G, S0>) run over blocks of 32 state rows staged in LDS
+// and accumulate in registers.
 template <int D>
 struct ChunkShape {
     static constexpr int R = D < 32 ? D : 32;   // state rows per block
@@ -353,111 +526,60 @@ struct ChunkShape {
     static constexpr int TPW = (NTD + 3) / 4;   // d tiles per wave
 };
 
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void backward_grad_kernel(
-    BwdIn in, const float* __restrict__ ck_s, const float* __restrict__ ck_ds, float* __restrict__ dq_h,
-    float* __restrict__ dk_h, float* __restrict__ dg, float* __restrict__ dbeta, float* __restrict__ dv) {
+    BwdIn in, const ChunkFac* __restrict__ fac, const float* __restrict__ ck_s, const float* __restrict__ ck_ds,
+    float* __restrict__ dq_h, float* __restrict__ dk_h, float* __restrict__ dg, float* __restrict__ dbeta,
+    float* __restrict__ dv) {
     using CS = ChunkShape<D>;
-    constexpr int C = kCkpt, R = CS::R, NB = CS::NB, KP = CS::KP, BP = CS::BP, NTD = CS::NTD, NTR = CS::NTR,
+    constexpr int C = kC, R = CS::R, NB = CS::NB, KP = CS::KP, BP = CS::BP, NTD = CS::NTD, NTR = CS::NTR,
                   TPW = CS::TPW;
     constexpr int SP = C + 1;   // pitch of the 16 x 16 matrices
     static_assert(C == 16 && R % 16 == 0, "chunk of 16 tokens, blocks of whole tiles");
     __shared__ __align__(16) float Kf[C][KP], Qf[C][KP];
     __shared__ __align__(16) float Sb[R][KP], Gb[R][KP];
     __shared__ float Vb[C][BP], dOb[C][BP], KSs[C][BP], KGs[C][BP], Us[C][BP], dUs[C][BP], Rs[C][BP];
-    __shared__ float At[C][SP], Pm[C][SP], Tm[C][SP], KK[C][SP], QK[C][SP], M4[C][SP], M5[C][SP], dOU[C][SP],
-        DUm[C][SP];
-    __shared__ float gin[C], gam[C], Gam[C], Gp[C], bet[C], part[4][3][C], red[4], dgs[C];
+    __shared__ float At[C][SP], Pm[C][SP], Tm[C][SP], M4[C][SP], M5[C][SP], dOU[C][SP], DUm[C][SP];
+    __shared__ float gam[C], Gam[C], Gp[C], bet[C], part[4][3][C], red[4], dgs[C];
 
-    const int h = blockIdx.x % in.num_v_heads;
-    const int64_t sl = blockIdx.x / in.num_v_heads;
-    int n = 0;
-    if (in.cu) {
-        int lo = 0, hi = in.num_seqs - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) / 2;
-            if (ckpt_base(in.cu, mid) <= sl) lo = mid;
-            else hi = mid - 1;
-        }
-        n = lo;
-    }
-    const int64_t bos = in.cu ? (int64_t)in.cu[n] : 0, eos = in.cu ? (int64_t)in.cu[n + 1] : in.total_tokens;
-    const int64_t j = sl - ckpt_base(in.cu, n);
-    if (j < 0 || j >= (eos - bos + C - 1) / C) return;   // a gap slot: uniform over the block
-    const int64_t t0 = bos + j * C;
-    const int cnt = (int)min((int64_t)C, eos - t0);
+    const int hv = in.num_v_heads, hqk = in.num_qk_heads, h = blockIdx.x % hv, hq = h / (hv / hqk);
+    const int64_t sl = blockIdx.x / hv;
+    int n, cnt;
+    int64_t t0;
+    if (!slot_chunk(in, sl, n, t0, cnt)) return;   // a gap slot: uniform over the block
     const int tid = threadIdx.x, w = tid / 64, ln = tid % 64, g4 = ln / 16, m = ln % 16;
-    const int hv = in.num_v_heads, hqk = in.num_qk_heads, hq = h / (hv / hqk);
     const float scale = in.scale;
     const int64_t off = (sl * hv + h) * (int64_t)D * D;
-    auto ld = [&](const void* p, int64_t idx) -> float {
-        if constexpr (BF16) return bf16_bits_to_float(reinterpret_cast<const uint16_t*>(p)[idx]);
-        else return reinterpret_cast<const float*>(p)[idx];
-    };
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    // Stage K, Q (rows past cnt are zero), g and beta.
-    for (int e = tid; e < C * D; e += 256) {
-        const int t = e / D, c = e % D;
-        const int64_t idx = ((t0 + min(t, cnt - 1)) * hqk + hq) * D + c;
-        const float keep = t < cnt ? 1.f : 0.f;
-        Kf[t][c] = keep * ld(in.k, idx);
-        Qf[t][c] = keep * ld(in.q, idx);
+    // Stage K, Q (rows past cnt are zero; thread tid: row tid / 16, D / 16 columns)
+    // and the chunk's factors.
+    {
+        constexpr int EPT = D / 16;
+        const int t = tid / 16, c0 = EPT * (tid % 16);
+        const int64_t idx = ((t0 + min(t, cnt - 1)) * hqk + hq) * D + c0;
+        float kv[EPT], qv[EPT];
+        ld_vec<BF16, EPT>(in.k, idx, kv);
+        ld_vec<BF16, EPT>(in.q, idx, qv);
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            Kf[t][c0 + i] = t < cnt ? kv[i] : 0.f;
+            Qf[t][c0 + i] = t < cnt ? qv[i] : 0.f;
+        }
     }
-    if (tid < C) {
-        const int64_t gi = (t0 + min(tid, cnt - 1)) * hv + h;
-        const float keep = tid < cnt ? 1.f : 0.f;
-        gin[tid] = keep * in.g[gi];
-        bet[tid] = keep * in.beta[gi];
-    }
-    __syncthreads();
-    // Decays (wave 0) and the Gram matrices K K^T (wave 1), Q K^T (wave 2).
-    if (w == 0) {
-        if (ln < C) {
-            float s = 0.f, tot = 0.f;
-            for (int t = 0; t < C; ++t) {
-                tot += gin[t];
-                if (t == ln) s = tot;
-            }
-            gam[ln] = s;
-            Gam[ln] = exp_nonpos(s);
-            Gp[ln] = exp_nonpos(tot - s);
+    {
+        const ChunkFac& F = fac[sl * hv + h];
+        const int r = tid / 16, c = tid % 16;
+        Tm[r][c] = F.T[r][c];
+        Pm[r][c] = F.P[r][c];
+        At[r][c] = F.At[r][c];
+        if (tid < C) {
+            gam[tid] = F.gam[tid];
+            bet[tid] = F.bet[tid];
+            Gam[tid] = F.Gam[tid];
+            Gp[tid] = F.Gp[tid];
         }
-    } else if (w <= 2) {
-        const float (*X)[KP] = w == 1 ? Kf : Qf;
-        f32x4 acc = zero4;
-        for (int kk = 0; kk < D / 4; ++kk) {
-            const int k = g4 * (D / 4) + kk;
-            acc = mfma4(X[m][k], Kf[m][k], acc);
-        }
-        float (*dst)[SP] = w == 1 ? KK : QK;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[4 * g4 + e][m] = acc[e];
-    }
-    __syncthreads();
-    // At, P and T = (I + diag(beta) At)^-1 (wave 0; lane c solves column c).
-    if (w == 0 && ln < C) {
-        const int c = ln;
-        for (int r = 0; r < C; ++r) {
-            const float dr = gam[r] - gam[c];
-            At[r][c] = c < r ? exp_nonpos(dr) * KK[r][c] : 0.f;
-            Pm[r][c] = c <= r ? exp_nonpos(dr) * QK[r][c] : 0.f;
-        }
-        float Tc[C];
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            float s = r == c ? 1.f : 0.f;
-            const float br = bet[r];
-#pragma unroll
-            for (int p = 0; p < r; ++p) s = fmaf(-br * At[r][p], Tc[p], s);
-            Tc[r] = s;
-        }
-#pragma unroll
-        for (int r = 0; r < C; ++r) Tm[r][c] = Tc[r];
     }
     // Accumulators over the blocks: U G, dO S0, dU S0 for this wave's d tiles; dO U^T
     // (wave 2) and dU U^T (wave 3); row sums for dbeta and du . AW; <G, S0>.
@@ -467,23 +589,39 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
     float p_db = 0.f, p_dw = 0.f, p_gs = 0.f;
     const int vt = tid / 16, vp = tid % 16;   // token and column phase for the row sums
 
+    // Rows of S0 and G of block rb + 1 on their way while block rb is processed.
+    constexpr int BV = (R * D + 4 * 256 - 1) / (4 * 256);   // f32x4 pieces per thread and matrix
+    f32x4 nS[BV], nG[BV];
+    auto load_block = [&](int rb) {
+        const float* s0 = ck_s + off + (int64_t)rb * R * D;
+        const float* gg = ck_ds + off + (int64_t)rb * R * D;
+#pragma unroll
+        for (int i = 0; i < BV; ++i) {
+            const int e = min(4 * tid + 4 * 256 * i, R * D - 4);
+            nS[i] = *reinterpret_cast<const f32x4*>(s0 + e);
+            nG[i] = *reinterpret_cast<const f32x4*>(gg + e);
+        }
+    };
+    load_block(0);
     for (int rb = 0; rb < NB; ++rb) {
-        __syncthreads();   // the previous block's LDS reads are done (and T is written)
+        __syncthreads();   // the previous block's LDS reads are done (and the factors are staged)
         // Stage this block's rows of S0 and G, and its columns of V and dO.
         {
-            const float* s0 = ck_s + off + (int64_t)rb * R * D;
-            const float* gg = ck_ds + off + (int64_t)rb * R * D;
-            for (int e = 4 * tid; e < R * D; e += 4 * 256) {
-                const int r = e / D, c = e % D;
-                *reinterpret_cast<f32x4*>(&Sb[r][c]) = *reinterpret_cast<const f32x4*>(s0 + e);
-                *reinterpret_cast<f32x4*>(&Gb[r][c]) = *reinterpret_cast<const f32x4*>(gg + e);
+#pragma unroll
+            for (int i = 0; i < BV; ++i) {
+                const int e = 4 * tid + 4 * 256 * i;
+                if (e < R * D) {
+                    *reinterpret_cast<f32x4*>(&Sb[e / D][e % D]) = nS[i];
+                    *reinterpret_cast<f32x4*>(&Gb[e / D][e % D]) = nG[i];
+                }
             }
+            if (rb + 1 < NB) load_block(rb + 1);
             for (int e = tid; e < C * R; e += 256) {
                 const int t = e / R, c = e % R;
                 const int64_t idx = ((t0 + min(t, cnt - 1)) * hv + h) * D + rb * R + c;
                 const float keep = t < cnt ? 1.f : 0.f;
-                Vb[t][c] = keep * ld(in.v, idx);
-                dOb[t][c] = keep * ld(in.dout, idx);
+                Vb[t][c] = keep * ld_in<BF16>(in.v, idx);
+                dOb[t][c] = keep * ld_in<BF16>(in.dout, idx);
             }
         }
         __syncthreads();
@@ -493,7 +631,7 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
             const int nt = tile % NTR;
             f32x4 acc = zero4;
             for (int kk = 0; kk < D / 4; ++kk) {
-                const int k = g4 * (D / 4) + kk;
+                const int k = 4 * kk + g4;
                 acc = mfma4(Kf[m][k], B[16 * nt + m][k], acc);
             }
             float (*dst)[BP] = tile < NTR ? KSs : KGs;
@@ -661,7 +799,7 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
                 }
             }
         }
-        dgs[t] = exp_nonpos(gam[C - 1]) * gs + a_excl + b_incl - c_excl + rect;
+        dgs[t] = Gam[C - 1] * gs + a_excl + b_incl - c_excl + rect;
     }
     __syncthreads();
     // Each token's 16-lane group holds its dbeta and du . AW sums.
@@ -703,60 +841,68 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
     }
 }
 
-// Pass 3, dq and dk of a QK head: the sum of the row-block parts of its V heads.
+// Pass 4, dq and dk of a QK head: the sum over its V heads.
 __global__ void backward_qk_sum_kernel(const float* __restrict__ part, float* __restrict__ dst, int64_t rows,
-                                       int32_t num_qk_heads, int32_t group, int32_t split, int32_t d) {
+                                       int32_t num_qk_heads, int32_t group, int32_t d) {
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // over rows * num_qk_heads * d
     if (e >= rows * num_qk_heads * d) return;
     const int64_t t = e / ((int64_t)num_qk_heads * d);
     const int64_t r = e % ((int64_t)num_qk_heads * d);
     const int hq = (int)(r / d), j = (int)(r % d);
-    const float* p = part + ((t * num_qk_heads + hq) * group) * (int64_t)split * d + j;
+    const float* p = part + ((t * num_qk_heads + hq) * group) * (int64_t)d + j;
     float s = 0.f;
-    for (int x = 0; x < group * split; ++x) s += p[(int64_t)x * d];
+    for (int x = 0; x < group; ++x) s += p[(int64_t)x * d];
     dst[e] = s;
 }
 
 size_t backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_v_heads, int32_t d) {
-    const int64_t slots = total_tokens / kCkpt + num_seqs;
-    const size_t ck = (size_t)slots * num_v_heads * d * d * sizeof(float);   // one checkpoint array
+    const int64_t slots = total_tokens / kC + num_seqs;
+    const size_t ck = (size_t)slots * num_v_heads * d * d * sizeof(float);    // one checkpoint array
     const size_t qk = (size_t)total_tokens * num_v_heads * d * sizeof(float);  // dq or dk per V head
-    return 2 * ck + 2 * qk;
+    const size_t fc = (size_t)slots * num_v_heads * sizeof(ChunkFac);
+    return 2 * ck + 2 * qk + fc;
 }
 
 template <int D, bool BF16>
 static hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t stream) {
-    using Sh = BwdShape<D>;
-    static_assert(Sh::SPLIT * Sh::ROWS == D && Sh::NT <= 512 && Sh::KPT * Sh::NT == kCkpt * D, "row blocks");
+    static_assert(sizeof(ChunkFac) % 16 == 0, "factor records keep the arrays after them aligned");
     float* ws = static_cast<float*>(a.workspace);
-    const int64_t slots = a.total_tokens / kCkpt + a.num_seqs;
+    const int64_t slots = a.total_tokens / kC + a.num_seqs;
     const size_t ck = (size_t)slots * a.num_v_heads * D * D;
     const size_t qk = (size_t)a.total_tokens * a.num_v_heads * D;
     float* ck_s = ws;
     float* ck_ds = ck_s + ck;
     float* dq_h = ck_ds + ck;
     float* dk_h = dq_h + qk;
+    ChunkFac* fac = reinterpret_cast<ChunkFac*>(dk_h + qk);
     const BwdIn in{a.q, a.k, a.v, a.d_out, a.g, a.beta, a.cu_seqlens, a.total_tokens,
                    a.num_seqs, a.num_qk_heads, a.num_v_heads, a.scale};
-    const int64_t P = (int64_t)a.num_seqs * a.num_v_heads * Sh::SPLIT;
+    const unsigned chunks = (unsigned)(slots * a.num_v_heads);
+    hipError_t e;
+    if (a.total_tokens > 0) {
+        prof::begin(stream, "gdn_backward_prep");
+        hipLaunchKernelGGL((backward_prep_kernel<D, BF16>), dim3(chunks), dim3(64), 0, stream, in, fac);
+        prof::end(stream);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const int64_t P = (int64_t)a.num_seqs * a.num_v_heads * (D / 16);
     prof::begin(stream, "gdn_backward_scan");
-    hipLaunchKernelGGL((backward_scan_kernel<D, BF16>), dim3((unsigned)(2 * P)), dim3(Sh::NT), 0, stream, in,
+    hipLaunchKernelGGL((backward_scan_kernel<D, BF16>), dim3((unsigned)(2 * P)), dim3(256), 0, stream, in, fac,
                        a.initial_state, a.d_final_state, a.d_initial_state, ck_s, ck_ds);
     prof::end(stream);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.total_tokens == 0) return e;
+    if ((e = hipGetLastError()) != hipSuccess || a.total_tokens == 0) return e;
     prof::begin(stream, "gdn_backward_grad");
-    hipLaunchKernelGGL((backward_grad_kernel<D, BF16>), dim3((unsigned)(slots * a.num_v_heads)), dim3(256), 0,
-                       stream, in, ck_s, ck_ds, dq_h, dk_h, a.dg, a.dbeta, a.dv);
+    hipLaunchKernelGGL((backward_grad_kernel<D, BF16>), dim3(chunks), dim3(256), 0, stream, in, fac, ck_s, ck_ds,
+                       dq_h, dk_h, a.dg, a.dbeta, a.dv);
     prof::end(stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nqk = a.total_tokens * a.num_qk_heads * D;
     const int group = a.num_v_heads / a.num_qk_heads;
     prof::begin(stream, "gdn_backward_sums");
     hipLaunchKernelGGL(backward_qk_sum_kernel, dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0, stream, dq_h, a.dq,
-                       a.total_tokens, a.num_qk_heads, group, 1, D);
+                       a.total_tokens, a.num_qk_heads, group, D);
     hipLaunchKernelGGL(backward_qk_sum_kernel, dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0, stream, dk_h, a.dk,
-                       a.total_tokens, a.num_qk_heads, group, 1, D);
+                       a.total_tokens, a.num_qk_heads, group, D);
     prof::end(stream);
     return hipGetLastError();
 }

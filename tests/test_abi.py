@@ -223,10 +223,12 @@ def test_backward_rejects(lib, over, status):
 
 def test_backward_workspace_size(lib):
     ws = gdn.gdn_backward_workspace_size
-    # state and state-gradient checkpoints per 16 tokens (plus one per sequence), then dq and dk
-    # per V head (summed over the V heads of each QK head at the end)
-    assert ws(4096, 1, 16, 32, 128, 128, gdn.GDN_BF16) == (2 * (4096 // 16 + 1) * 32 * 128 * 128 * 4
-                                                          + 2 * 4096 * 32 * 128 * 4)
+    # state and state-gradient checkpoints per 16-token chunk (plus one per sequence), dq and dk
+    # per V head (summed over the V heads of each QK head at the end), and per chunk and V head
+    # its factors (four 16-vectors and three 16 x 16 matrices in fp32: 3328 bytes)
+    slots = 4096 // 16 + 1
+    assert ws(4096, 1, 16, 32, 128, 128, gdn.GDN_BF16) == (2 * slots * 32 * 128 * 128 * 4
+                                                          + 2 * 4096 * 32 * 128 * 4 + slots * 32 * 3328)
     assert ws(100, 1, 3, 32, 128, 128, gdn.GDN_BF16) == 0
 
 
