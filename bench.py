@@ -25,8 +25,8 @@ Roofline figures use algorithmic work only:
       256 sequences: the state read and written once plus 4 tokens' inputs and
       outputs, 1,099,169,792 bytes per step
   backward ("backward"): gradients of the prefill on the T = 4096 layer shape,
-      against the fp32 vector peak (157.3 TFLOP/s) at 17 d^2 flop per token and
-      V head (the recomputation of forward states not counted)
+      against the fp32 peak (157.3 TFLOP/s) at 17 d^2 flop per token and V head
+      (the recomputation of forward states not counted), over its four kernels
   with q and k L2-normalised in the kernels ("prefill_qk_l2norm",
       "decode.qk_l2norm"): the same inputs and algorithmic work
 Peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8.0 TB/s.
@@ -416,14 +416,14 @@ def main():
 
         bsteps = max(2, args.steps // 4)
         bms, bkern = time_calls(backward, bsteps, 2, torch)
-        # three stages per call: the two scans, the per-interval gradients, the fixed-order sums
-        bparts = {k: bkern[k][1] for k in ("gdn_backward_scan", "gdn_backward_grad", "gdn_backward_sums")
-                  if k in bkern}
+        # four stages per call: chunk factors, the two scans, the per-chunk gradients, the fixed-order sums
+        bparts = {k: bkern[k][1] for k in ("gdn_backward_prep", "gdn_backward_scan", "gdn_backward_grad",
+                                            "gdn_backward_sums") if k in bkern}
         bkms = sum(bparts.values()) or bms
         btf = BACKWARD_FLOP_PER_TOKEN * xb.T / (bkms / 1e3) / 1e12
         result["backward"] = {"workload": "qwen3next_gdn_backward_T4096", "steps": bsteps, "ms_per_step": bms,
                               "kernel_ms_per_launch": bparts, "tokens_per_s": xb.T / (bms / 1e3),
-                              "roofline": {"kernel": "gdn_backward_scan+grad+sums", "bound": "alu",
+                              "roofline": {"kernel": "gdn_backward_prep+scan+grad+sums", "bound": "alu",
                                            "achieved": btf,
                                            "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
                                            "frac": btf / PEAK_FP32_VECTOR_TFLOPS}}

@@ -274,14 +274,15 @@ gdn_status_t gdn_decode_ex(const void* q, const void* k, const void* v,
  *   dv              [total_tokens, num_v_heads, d_v]
  *   dg, dbeta       [total_tokens, num_v_heads]         (dg: with respect to g = log alpha)
  *   d_initial_state [num_seqs, num_v_heads, d_v, d_k], or NULL
- * The computation is token by token in fp32. Two scans (forward and reverse,
- * rows of each state split over blocks of 32) store the state and its gradient
- * every 16 tokens in the workspace; then every 16-token interval is handled in
- * parallel, rebuilding the state before each token from its checkpoint and
- * writing per-row-block parts of dq, dk, dg and dbeta to the workspace; a last
- * pass adds the parts in a fixed order, so results are deterministic.
- * workspace: gdn_backward_workspace_size(...) bytes; for d = d_k = d_v >= 32
- * about 8 d^2 Hv (T / 16 + N) + (8 d + 8) Hv T d / 32 bytes.
+ * The computation is in fp32 by chunks of 16 tokens, each chunk's token rule
+ * unrolled into closed form (triangular solve and matrix products on fp32
+ * MFMA): a pass builds every chunk's factors, two scans (forward and reverse,
+ * 16 state rows per workgroup) store the state before and the state gradient
+ * after every chunk in the workspace, every chunk's gradients then follow in
+ * parallel from those two, and a last pass sums dq and dk over the V heads of
+ * each QK head in a fixed order, so results are deterministic.
+ * workspace: gdn_backward_workspace_size(...) bytes, for d = d_k = d_v:
+ * 8 d^2 Hv (T / 16 + N) + 8 d Hv T + 3328 Hv (T / 16 + N).
  */
 size_t gdn_backward_workspace_size(int64_t total_tokens, int32_t num_seqs,
                                    int32_t num_qk_heads, int32_t num_v_heads,
