@@ -46,3 +46,28 @@ def test_backward(dtype, d, lengths, with_dfinal):
         e = rel_l2(res[mine].cpu().numpy(), ref[theirs])
         log(f"[parity] {x.name} {mine}: rel={e:.3e}")
         assert e <= TOL, (mine, e)
+
+
+def test_backward_layer_heads():
+    """The layer's own head layout (16 QK heads shared by 32 V heads, d = 128, scale 1/sqrt(d)),
+    two ragged sequences with initial states and a final-state gradient: 32 chunks of 16 tokens
+    over the scans, the per-chunk gradients and the sums over the V heads of each QK head."""
+    lengths = [300, 212]
+    x = I.draw(lengths=lengths, hqk=16, hv=32, dk=128, dtype="bf16", seed=431, s0_std=0.1,
+               scale=128 ** -0.5, name="backward_layer_heads")
+    rng = np.random.default_rng(432)
+    d_out_in = I.f32_to_bf16_bits(rng.standard_normal(x.v.shape).astype(np.float32))
+    d_out = oracle.upcast(d_out_in)
+    d_fin = rng.standard_normal(x.s0.shape).astype(np.float32)
+    dev = to_device(x)
+    log(f"[gpu] gdn_backward {x.name} T={x.T} lengths={lengths} heads 16/32")
+    res = gdn.gdn_backward(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
+                           torch.from_numpy(d_out_in).view(torch.bfloat16).cuda(), dev["s0"], dev["cu"],
+                           torch.from_numpy(d_fin).cuda(), scale=x.scale)
+    torch.cuda.synchronize()
+    ref = oracle.backward(x.q, x.k, x.v, x.g, x.beta, x.s0, x.cu_seqlens, d_out, d_fin, scale=x.scale)
+    for mine, theirs in [("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dg", "dg"), ("dbeta", "dbeta"),
+                         ("d_initial_state", "ds0")]:
+        e = rel_l2(res[mine].cpu().numpy(), ref[theirs])
+        log(f"[parity] {x.name} {mine}: rel={e:.3e}")
+        assert e <= TOL, (mine, e)
