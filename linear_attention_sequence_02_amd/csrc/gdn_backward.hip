@@ -540,7 +540,7 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
     __shared__ __align__(16) float Kf[C][KP], Qf[C][KP];
     __shared__ __align__(16) float Sb[R][KP], Gb[R][KP];
     __shared__ float Vb[C][BP], dOb[C][BP], KSs[C][BP], KGs[C][BP], Us[C][BP], dUs[C][BP], Rs[C][BP];
-    __shared__ float At[C][SP], Pm[C][SP], Tm[C][SP], M4[C][SP], M5[C][SP], dOU[C][SP], DUm[C][SP];
+    __shared__ float At[C][SP], Pm[C][SP], Tm[C][SP], M4[C][SP], M5[C][SP], dOU[C][SP], DUm[C][SP], Rm[C][SP];
     __shared__ float gam[C], Gam[C], Gp[C], bet[C], part[4][3][C], red[4], dgs[C];
 
     const int hv = in.num_v_heads, hqk = in.num_qk_heads, h = blockIdx.x % hv, hq = h / (hv / hqk);
@@ -589,9 +589,12 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
     float p_db = 0.f, p_dw = 0.f, p_gs = 0.f;
     const int vt = tid / 16, vp = tid % 16;   // token and column phase for the row sums
 
-    // Rows of S0 and G of block rb + 1 on their way while block rb is processed.
+    // Rows of S0 and G, and columns of V and dO, of block rb + 1 on their way while
+    // block rb is processed (raw words, converted when written to LDS).
     constexpr int BV = (R * D + 4 * 256 - 1) / (4 * 256);   // f32x4 pieces per thread and matrix
+    constexpr int VV = (C * R + 255) / 256;                 // V (and dO) elements per thread
     f32x4 nS[BV], nG[BV];
+    Raw<BF16, 1> nV[VV], nO[VV];
     auto load_block = [&](int rb) {
         const float* s0 = ck_s + off + (int64_t)rb * R * D;
         const float* gg = ck_ds + off + (int64_t)rb * R * D;
@@ -600,6 +603,13 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
             const int e = min(4 * tid + 4 * 256 * i, R * D - 4);
             nS[i] = *reinterpret_cast<const f32x4*>(s0 + e);
             nG[i] = *reinterpret_cast<const f32x4*>(gg + e);
+        }
+#pragma unroll
+        for (int i = 0; i < VV; ++i) {
+            const int e = min(tid + 256 * i, C * R - 1), t = e / R, c = e % R;
+            const int64_t idx = ((t0 + min(t, cnt - 1)) * hv + h) * D + rb * R + c;
+            ld_raw<BF16, 1>(in.v, idx, nV[i]);
+            ld_raw<BF16, 1>(in.dout, idx, nO[i]);
         }
     };
     load_block(0);
@@ -615,14 +625,15 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
                     *reinterpret_cast<f32x4*>(&Gb[e / D][e % D]) = nG[i];
                 }
             }
-            if (rb + 1 < NB) load_block(rb + 1);
-            for (int e = tid; e < C * R; e += 256) {
-                const int t = e / R, c = e % R;
-                const int64_t idx = ((t0 + min(t, cnt - 1)) * hv + h) * D + rb * R + c;
-                const float keep = t < cnt ? 1.f : 0.f;
-                Vb[t][c] = keep * ld_in<BF16>(in.v, idx);
-                dOb[t][c] = keep * ld_in<BF16>(in.dout, idx);
+#pragma unroll
+            for (int i = 0; i < VV; ++i) {
+                const int e = tid + 256 * i, t = e / R, c = e % R;
+                if (e < C * R) {
+                    Vb[t][c] = t < cnt ? raw_at(nV[i], 0) : 0.f;
+                    dOb[t][c] = t < cnt ? raw_at(nO[i], 0) : 0.f;
+                }
             }
+            if (rb + 1 < NB) load_block(rb + 1);
         }
         __syncthreads();
         // K S0^T and K G^T for the block's columns: 2 NTR tiles.
@@ -767,39 +778,37 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
     p_gs = swap32_sum(p_gs);
     if (ln == 0) red[w] = p_gs;
     __syncthreads();
-    // M4 and M5 (wave 0, lane t builds row t); dg and dbeta (wave 1, lane t).
-    if (w == 0 && ln < C) {
-        const int t = ln;
-        const float bt = bet[t];
-        for (int s = 0; s < C; ++s) {
-            const float dts = gam[t] - gam[s];
-            M4[t][s] = s <= t ? exp_nonpos(dts) * dOU[t][s] : 0.f;
-            float m5 = 0.f;
-            if (s > t) m5 = exp_nonpos(-dts) * bet[s] * DUm[s][t];
-            if (s < t) m5 = bt * exp_nonpos(dts) * DUm[t][s];
-            M5[t][s] = m5;
+    // M4, M5 and the dg terms, one thread per (row s, column t) of the 16 x 16
+    // matrices: thread (s, t) builds M4[s][t], M5[s][t] and row s's share of
+    // token t's dg; the shares are then summed per token.
+    {
+        const int sr = tid / 16, tc = tid % 16;
+        const float drc = gam[sr] - gam[tc];
+        M4[sr][tc] = tc <= sr ? exp_nonpos(drc) * dOU[sr][tc] : 0.f;
+        float m5 = 0.f;
+        if (tc > sr) m5 = exp_nonpos(-drc) * bet[tc] * DUm[tc][sr];
+        if (tc < sr) m5 = bet[sr] * exp_nonpos(drc) * DUm[sr][tc];
+        M5[sr][tc] = m5;
+        const float a = Gp[sr] * (part[0][0][sr] + part[1][0][sr] + part[2][0][sr] + part[3][0][sr]);
+        const float b = scale * Gam[sr] * (part[0][1][sr] + part[1][1][sr] + part[2][1][sr] + part[3][1][sr]);
+        const float c3 = Gam[sr] * bet[sr] * (part[0][2][sr] + part[1][2][sr] + part[2][2][sr] + part[3][2][sr]);
+        // rectangle terms of row s >= t: sum over tau < t
+        float r1 = 0.f, r2 = 0.f;
+#pragma unroll
+        for (int tau = 0; tau < C; ++tau) {
+            const float on = tau < tc ? 1.f : 0.f;
+            r1 = fmaf(on * Pm[sr][tau], dOU[sr][tau], r1);
+            r2 = fmaf(on * At[sr][tau], DUm[sr][tau], r2);
         }
+        float x = (sr < tc ? a : 0.f) - (sr > tc ? c3 + bet[sr] * r2 : 0.f);
+        if (sr >= tc) x += b + scale * r1;
+        Rm[sr][tc] = x;
     }
-    if (w == 1 && ln < C) {
-        const int t = ln;
-        const float gs = red[0] + red[1] + red[2] + red[3];
-        float a_excl = 0.f, b_incl = 0.f, c_excl = 0.f, rect = 0.f;
-        for (int s = 0; s < C; ++s) {
-            const float a = Gp[s] * (part[0][0][s] + part[1][0][s] + part[2][0][s] + part[3][0][s]);
-            const float b = scale * Gam[s] * (part[0][1][s] + part[1][1][s] + part[2][1][s] + part[3][1][s]);
-            const float cc = Gam[s] * bet[s] * (part[0][2][s] + part[1][2][s] + part[2][2][s] + part[3][2][s]);
-            if (s < t) a_excl += a;
-            if (s >= t) b_incl += b;
-            if (s > t) c_excl += cc;
-            if (s >= t) {
-                for (int tau = 0; tau < t; ++tau) {
-                    float x = scale * Pm[s][tau] * dOU[s][tau];
-                    if (s > t) x -= bet[s] * At[s][tau] * DUm[s][tau];
-                    rect += x;
-                }
-            }
-        }
-        dgs[t] = Gam[C - 1] * gs + a_excl + b_incl - c_excl + rect;
+    __syncthreads();
+    if (tid < C) {
+        float sum = 0.f;
+        for (int sr = 0; sr < C; ++sr) sum += Rm[sr][tid];
+        dgs[tid] = Gam[C - 1] * (red[0] + red[1] + red[2] + red[3]) + sum;
     }
     __syncthreads();
     // Each token's 16-lane group holds its dbeta and du . AW sums.
