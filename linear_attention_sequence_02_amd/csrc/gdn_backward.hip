@@ -675,7 +675,8 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
                 KGs[t][c] = fmaf(Gp[t], KGs[t][c], scale * acc[e]);   // Y = Gp K G^T + scale P^T dO
             }
         }
-        __syncthreads();
+        // Each wave next reads only the columns of U (or Y) it has just written.
+        wave_lds_sync();
         // AW = Gam K S0^T + At U, R = V - AW (waves 0 ..); dU = T^T Y (waves 2 ..).
         if (w < NTR) {
             const int c = 16 * w + m;
