@@ -71,3 +71,20 @@ def test_backward_layer_heads():
         e = rel_l2(res[mine].cpu().numpy(), ref[theirs])
         log(f"[parity] {x.name} {mine}: rel={e:.3e}")
         assert e <= TOL, (mine, e)
+
+
+def test_backward_no_tokens():
+    """No tokens in any sequence: the gradient of each initial state is the gradient of its final
+    state (the recurrence is the identity), and the token gradients are empty."""
+    n, hqk, hv, d = 3, 1, 2, 32
+    rng = np.random.default_rng(441)
+    d_fin = torch.from_numpy(rng.standard_normal((n, hv, d, d)).astype(np.float32)).cuda()
+    s0 = torch.from_numpy(rng.standard_normal((n, hv, d, d)).astype(np.float32)).cuda()
+    z = lambda *shape: torch.zeros(shape, dtype=torch.float32, device="cuda")
+    cu = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+    log("[gpu] gdn_backward no tokens, 3 sequences")
+    res = gdn.gdn_backward(z(0, hqk, d), z(0, hqk, d), z(0, hv, d), z(0, hv), z(0, hv), z(0, hv, d), s0, cu, d_fin)
+    torch.cuda.synchronize()
+    assert torch.equal(res["d_initial_state"], d_fin)
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert res[name].shape[0] == 0
