@@ -259,8 +259,8 @@ __global__ __launch_bounds__(64) void backward_prep_kernel(BwdIn in, ChunkFac* _
 // That layout is also the B operand of K S0^T when step (tk, e) takes, in lane
 // group g, key 16 tk + 4 g + e, so the state never leaves the registers; each
 // wave adds its key tiles' share of K S0^T (or K G^T) and the shares meet in LDS,
-// one barrier per chunk. The inputs of the next chunks are loaded into
-// registers one chunk ahead and kept in a ring of three LDS buffers.
+// one barrier per chunk. The inputs of later chunks are loaded into two
+// register sets ahead of use and kept in a ring of three LDS buffers.
 template <int D>
 struct ScanShape {
     static constexpr int NTD = D / 16;            // 16-wide tiles over d
