@@ -32,6 +32,7 @@
 // LDS banks; a contraction may also take its k in any other order that A and B share.
 #include "gdn_common.h"
 #include "gdn_internal.h"
+#include "gdn_mfma.h"
 
 namespace gdn {
 
@@ -362,6 +363,11 @@ __device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, cons
             acc[i] = (src && tk < NTD) ? *reinterpret_cast<const f32x4*>(src + row * D + 16 * tk + 4 * g4)
                                        : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        // Let these loads finish here, once: otherwise the compiler, unable to
+        // tell whether they are still in flight when the chunk loop starts, waits
+        // for every outstanding load (the prefetch included) at each use of the
+        // state inside the loop.
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unconstrained
     }
     // Chunks q and q + 1 sit in LDS when chunk q starts; two register sets hold
     // chunks q + 2 and q + 3 on their way (loaded two chunks ahead of use).
@@ -374,7 +380,7 @@ __device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, cons
         fetch(pb, 1);
         commit(pb, 1);
     }
-    __syncthreads();
+    mf::lds_barrier();
     if (nint > 2) fetch(pa, 2);
     if (nint > 3) fetch(pb, 3);
     auto chunk = [&](int q, Pre& pre) {
@@ -406,7 +412,7 @@ __device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, cons
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) z = mfma4(Pc[bb][4 * kk + g4][m], Xc[bb][4 * kk + g4][m], z);
         }
-        __syncthreads();
+        mf::lds_barrier();
         // Buffer (q + 2) % 3 was last read in chunk q - 1, which every wave has finished.
         if (q + 2 < nint) commit(pre, (q + 2) % 3);
         if (q + 4 < nint) fetch(pre, q + 4);
@@ -614,7 +620,7 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
     };
     load_block(0);
     for (int rb = 0; rb < NB; ++rb) {
-        __syncthreads();   // the previous block's LDS reads are done (and the factors are staged)
+        mf::lds_barrier();   // the previous block's LDS reads are done (and the factors are staged)
         // Stage this block's rows of S0 and G, and its columns of V and dO.
         {
 #pragma unroll
@@ -635,7 +641,7 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
             }
             if (rb + 1 < NB) load_block(rb + 1);
         }
-        __syncthreads();
+        mf::lds_barrier();
         // K S0^T and K G^T for the block's columns: 2 NTR tiles.
         for (int tile = w; tile < 2 * NTR; tile += 4) {
             const float (*B)[KP] = tile < NTR ? Sb : Gb;
@@ -649,7 +655,7 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) dst[4 * g4 + e][16 * nt + m] = acc[e];
         }
-        __syncthreads();
+        mf::lds_barrier();
         // U (waves 0 .. NTR - 1) and Z = P^T dO (waves 2 .. 2 + NTR - 1).
         if (w < NTR) {
             const int c = 16 * w + m;
@@ -702,7 +708,7 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) dUs[4 * g4 + e][c] = acc[e];
         }
-        __syncthreads();
+        mf::lds_barrier();
         // dv, the row sums and <G, S0> on the block.
         for (int c = vp; c < R; c += 16) {
             const float du = dUs[vt][c], r = Rs[vt][c];
@@ -778,7 +784,7 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
     p_gs = swap16_sum(p_gs);
     p_gs = swap32_sum(p_gs);
     if (ln == 0) red[w] = p_gs;
-    __syncthreads();
+    mf::lds_barrier();
     // M4, M5 and the dg terms, one thread per (row s, column t) of the 16 x 16
     // matrices: thread (s, t) builds M4[s][t], M5[s][t] and row s's share of
     // token t's dg; the shares are then summed per token.
@@ -805,13 +811,13 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
         if (sr >= tc) x += b + scale * r1;
         Rm[sr][tc] = x;
     }
-    __syncthreads();
+    mf::lds_barrier();
     if (tid < C) {
         float sum = 0.f;
         for (int sr = 0; sr < C; ++sr) sum += Rm[sr][tid];
         dgs[tid] = Gam[C - 1] * (red[0] + red[1] + red[2] + red[3]) + sum;
     }
-    __syncthreads();
+    mf::lds_barrier();
     // Each token's 16-lane group holds its dbeta and du . AW sums.
     if (vp == 0 && vt < cnt) {
         const int64_t gi = (t0 + vt) * hv + h;
