@@ -120,6 +120,14 @@ def test_prefill_bf16_qwen_layer_T4096():
     _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
 
 
+def test_prefill_bf16_qwen_layer_T65536():
+    # The timed prefill workload itself (same seed, same launches: 114-chunk segments, 9 per head);
+    # the C oracle covers all 65,536 tokens of every head in a few seconds.
+    x = I.qwen3_next_prefill(T=65536)
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
+
+
 def test_prefill_bf16_varlen8():
     x = I.varlen_prefill()
     out, fin = run_prefill(x)
