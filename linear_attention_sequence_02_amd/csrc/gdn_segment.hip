@@ -398,11 +398,12 @@ __device__ __forceinline__ void chain_fetch_v(uint32_t (&vr)[16], const uint16_t
 
 // One chunk of one chain for this wave's 32 value columns; lane (g, m) holds
 // columns cb + 2 m (tile nt = 0) and cb + 2 m + 1 (nt = 1). ST[t][nt] element e
-// is S[column][key 16 t + 4 g + e]. vr holds this chunk's values on entry and
-// the next chunk's (from vnext) on return.
+// is S[column][key 16 t + 4 g + e]. vin holds this chunk's values; the next
+// chunk's (from vnext) are requested into vout.
 template <bool WITH_V, bool WITH_OUT>
 __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q, const ChunkFactors& F,
-                                           f32x4 (&ST)[8][2], uint32_t (&vr)[16], const uint16_t* vnext, int ncn,
+                                           f32x4 (&ST)[8][2], const uint32_t (&vin)[16], uint32_t (&vout)[16],
+                                           const uint16_t* vnext, int ncn,
                                            uint16_t* orow0, int ldv, int nc, float scale, int g, int m) {
     // Z = K S^T and, for the output, Y = Q S^T: one pass over the S^T operands.
     f32x4 X[4][2], Y[4][2];
@@ -468,8 +469,8 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
         for (int e = 0; e < 4; ++e) {
             float v0 = 0.f, v1 = 0.f;
             if (WITH_V) {
-                v0 = __uint_as_float(vr[4 * mt + e] << 16);
-                v1 = __uint_as_float(vr[4 * mt + e] & 0xFFFF0000u);
+                v0 = __uint_as_float(vin[4 * mt + e] << 16);
+                v1 = __uint_as_float(vin[4 * mt + e] & 0xFFFF0000u);
             }
             X[mt][0][e] = Br[e] * (v0 - Gr[e] * X[mt][0][e]);
             X[mt][1][e] = Br[e] * (v1 - Gr[e] * X[mt][1][e]);
@@ -479,7 +480,7 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
     // consumed: global loads complete in order, so a load hoisted above the
     // uses of the previous ones would make those uses wait for it.
     __builtin_amdgcn_sched_barrier(0);
-    if (WITH_V) chain_fetch_v(vr, vnext, ncn, ldv, g, m);
+    if (WITH_V) chain_fetch_v(vout, vnext, ncn, ldv, g, m);
     // U by 16-row blocks: U_b = Td_b (X_b - sum A_bb' U_b'), and the state
     // update's exp(gamma_last - gamma) U_b = Tw_b (same right-hand side),
     // packed as soon as a pair of blocks is done.
@@ -561,32 +562,48 @@ __device__ __forceinline__ void chain_loop(SegSmem<MODE>& sm, f32x4 (&ST)[8][2],
         const int64_t rem = eos - (bos + c * kChunk);
         return (int)(rem < kChunk ? rem : kChunk);
     };
-    uint32_t vr[16];
-    if (nchunks > 0) chain_fetch_v(vr, vcol + (bos + c_begin * kChunk) * ldv, chunk_nc(c_begin), ldv, lg, lm);
+    uint32_t va[16];
+    if (nchunks > 0) chain_fetch_v(va, vcol + (bos + c_begin * kChunk) * ldv, chunk_nc(c_begin), ldv, lg, lm);
     // The entry state and the first values have arrived before the chunk loop
     // starts; otherwise the loop header's wait for the values would also cover
     // every later global access (the previous chunk's output stores included).
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     lds_barrier();   // prologue: chunks 0 and 1 staged
     lds_barrier();   // prologue: chunk 0's factors
-    for (int64_t i = 0; i < nchunks; ++i) {
-        const int64_t c = c_begin + i;
-        const int kb = (int)(i % 3);
-        const int64_t cn = (i + 1 < nchunks) ? c + 1 : c;
-        const int64_t t0 = bos + c * kChunk;
-        const uint16_t* vnext = vcol + (bos + cn * kChunk) * ldv;
-        if (MODE == kModeOut) {
-            chain_step<true, true>(&sm.K[kb][0][0], &sm.Q[kb][0][0], sm.F[i & 1], ST, vr, vnext, chunk_nc(cn),
+    if constexpr (MODE == kModeOut) {
+        for (int64_t i = 0; i < nchunks; ++i) {
+            const int64_t c = c_begin + i;
+            const int kb = (int)(i % 3);
+            const int64_t cn = (i + 1 < nchunks) ? c + 1 : c;
+            const int64_t t0 = bos + c * kChunk;
+            const uint16_t* vnext = vcol + (bos + cn * kChunk) * ldv;
+            chain_step<true, true>(&sm.K[kb][0][0], &sm.Q[kb][0][0], sm.F[i & 1], ST, va, va, vnext, chunk_nc(cn),
                                    ocol + t0 * ldv, ldv, chunk_nc(c), scale, lg, lm);
-        } else {
-            chain_step<true, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], ST, vr, vnext, chunk_nc(cn), nullptr, ldv,
-                                    chunk_nc(c), scale, lg, lm);
+            lds_barrier();
+        }
+    } else {
+        // Map pass: two value register sets, the loop unrolled by two, so that
+        // the values requested during chunk i land in the set chunk i + 1
+        // reads (with one set, register copies at the loop's back edge waited
+        // for them before each chunk's barrier).
+        uint32_t vb[16];
+        auto chunk = [&](int64_t i, const uint32_t (&vin)[16], uint32_t (&vout)[16]) {
+            const int64_t c = c_begin + i;
+            const int kb = (int)(i % 3);
+            const int64_t cn = (i + 1 < nchunks) ? c + 1 : c;
+            const uint16_t* vnext = vcol + (bos + cn * kChunk) * ldv;
+            chain_step<true, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], ST, vin, vout, vnext, chunk_nc(cn),
+                                    nullptr, ldv, chunk_nc(c), scale, lg, lm);
             __builtin_amdgcn_sched_barrier(0);   // keep the H and M steps' temporaries apart
             if (with_m)
-                chain_step<false, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], SM, vr, nullptr, 0, nullptr, ldv,
-                                         chunk_nc(c), scale, lg, lm);
+                chain_step<false, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], SM, vout, vout, nullptr, 0, nullptr,
+                                         ldv, chunk_nc(c), scale, lg, lm);
+            lds_barrier();
+        };
+        for (int64_t i = 0; i < nchunks; i += 2) {
+            chunk(i, va, vb);
+            if (i + 1 < nchunks) chunk(i + 1, vb, va);
         }
-        lds_barrier();
     }
 }
 
