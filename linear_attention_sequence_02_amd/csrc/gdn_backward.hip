@@ -519,11 +519,12 @@ __global__ __launch_bounds__(256) void backward_scan_kernel(
 //          - sum_{s > t, tau < t} beta_s At[s][tau] (dU U^T)[s][tau] - beta_t du_t . AW_t,
 //   a = Gp (U G . K), b = scale Gam (dO S0 . Q), c = Gam beta (dU S0 . K) (row dots),
 // dec[r][c] = exp(gamma_r - gamma_c). Products over the value index (U G, dO S0,
-// dU S0, dO U^T, dU U^T, <G, S0>) run over blocks of 32 state rows staged in LDS
-// and accumulate in registers.
+// dU S0, dO U^T, dU U^T, <G, S0>) run over blocks of 16 state rows staged in LDS
+// and accumulate in registers (16-row blocks keep the LDS at 52 KB for d = 128,
+// so three workgroups share a CU).
 template <int D>
 struct ChunkShape {
-    static constexpr int R = D < 32 ? D : 32;   // state rows per block
+    static constexpr int R = 16;                // state rows per block
     static constexpr int NB = D / R;            // blocks
     static constexpr int KP = D + 4;            // fp32 row pitch of d-wide rows
     static constexpr int BP = R + 4;            // fp32 row pitch of block-wide rows
