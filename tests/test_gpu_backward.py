@@ -73,6 +73,29 @@ def test_backward_layer_heads():
         assert e <= TOL, (mine, e)
 
 
+def test_backward_layer_T4096_sampled_head():
+    """The timed backward workload itself (T = 4096, 16 QK / 32 V heads, bf16, zero initial state,
+    d_out the values drawn with seed 1007) in its own launch configuration; the oracle recomputes
+    QK head 5 and its two V heads (heads are independent: a QK head's gradient depends only on the
+    V heads that share it)."""
+    x = I.qwen3_next_prefill(T=4096)
+    d_out_in = I.draw(T=4096, hqk=x.hqk, hv=x.hv, dk=x.dk, seed=1007).v
+    dev = to_device(x)
+    log(f"[gpu] gdn_backward {x.name} T={x.T} heads 16/32")
+    res = gdn.gdn_backward(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
+                           torch.from_numpy(d_out_in).view(torch.bfloat16).cuda(), None, None, scale=x.scale)
+    torch.cuda.synchronize()
+    hq, hv = 5, slice(10, 12)
+    ref = oracle.backward(x.q[:, hq:hq + 1], x.k[:, hq:hq + 1], x.v[:, hv], x.g[:, hv], x.beta[:, hv], None, None,
+                          oracle.upcast(d_out_in)[:, hv], None, scale=x.scale)
+    mine = {"dq": res["dq"][:, hq:hq + 1], "dk": res["dk"][:, hq:hq + 1], "dv": res["dv"][:, hv],
+            "dg": res["dg"][:, hv], "dbeta": res["dbeta"][:, hv], "ds0": res["d_initial_state"][:, hv]}
+    for name, t in mine.items():
+        e = rel_l2(t.cpu().numpy(), ref[name])
+        log(f"[parity] {x.name} {name}: rel={e:.3e}")
+        assert e <= TOL, (name, e)
+
+
 def test_backward_no_tokens():
     """No tokens in any sequence: the gradient of each initial state is the gradient of its final
     state (the recurrence is the identity), and the token gradients are empty."""
