@@ -36,7 +36,7 @@ per-kernel instrumentation; the per-kernel launch times come from a separate
 run of the same number of steps. "parity" is the rel-L2 (fp64) of the timed
 run's output, and of its final state when the oracle sample covers the
 whole input, against the fp64 oracle run for "cpu_baseline" on the same
-inputs.
+inputs ("cpu_baseline" also gives the oracle on one core and the host CPU model).
 HBM traffic per launch ("traffic") comes from rocprofv3 FETCH_SIZE and
 WRITE_SIZE passes recorded in profiles/traffic.json, scaled by the same
 counters read for a plain device copy of known size (--calibration-copy); it
@@ -203,7 +203,25 @@ def cpu_baseline(x, budget_s=20.0):
     base = {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {T} of {x.T} tokens of the same input, all {x.hv} V heads, fp64 recurrence, "
                       f"{dt:.1f} s"}
+    # The same oracle on one core, over a shorter prefix (about a second of work).
+    T1 = max(16, min(x.T, int(T / dt / max(int(threads), 1))))
+    t0 = time.perf_counter()
+    oracle.recurrent(x.q[:T1], x.k[:T1], x.v[:T1], x.g[:T1], x.beta[:T1], None, None, scale=x.scale, threads=1)
+    base["one_core"] = {"value": T1 / (time.perf_counter() - t0), "unit": "tokens/s", "sample": f"first {T1} tokens"}
+    base["cpu_model"] = cpu_model()
     return base, T, o_ref, (s_ref if T == x.T else None)
+
+
+def cpu_model():
+    """The host CPU's model name as the kernel reports it (None where /proc/cpuinfo has none)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def rel_l2(a, ref):
