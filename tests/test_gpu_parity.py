@@ -114,6 +114,16 @@ def test_prefill_bf16_many_short_sequences():
     _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
 
 
+def test_prefill_bf16_thousand_tiny_sequences():
+    # 1,000 sequences of 0-130 tokens (empty, single-token and chunk-boundary lengths among them),
+    # with initial states: the segment slot indexing and the many-chain launch at scale.
+    lengths = [int(x) for x in np.random.default_rng(89).integers(0, 131, size=1000)]
+    lengths[:6] = [0, 1, 63, 64, 65, 128]
+    x = I.draw(lengths=lengths, hqk=2, hv=4, dk=128, dtype="bf16", seed=89, s0_std=0.1, name="bf16_1000_tiny")
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
+
+
 def test_prefill_bf16_qwen_layer_T4096():
     x = I.qwen3_next_prefill(T=4096)
     out, fin = run_prefill(x)
