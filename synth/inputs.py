@@ -274,6 +274,15 @@ def chunk_count(lengths, chunk: int = 64) -> int:
     return int(sum(math.ceil(L / chunk) for L in lengths))
 
 
+def large_state(num: int, hv: int, d: int, seed: int, std: float = 0.01) -> np.ndarray:
+    """States [num, hv, d, d] fp32 = std * N(0, 1), drawn in fp32 from default_rng(seed) (no fp64
+    temporary: for state arrays of several GiB)."""
+    rng = np.random.default_rng(seed)
+    out = rng.standard_normal((num, hv, d, d), dtype=np.float32)
+    out *= np.float32(std)
+    return out
+
+
 def state_pool(num_slots: int, hv: int, d: int, seed: int, std: float = 0.3) -> np.ndarray:
     """A state pool [num_slots, hv, d, d] fp32 = std * N(0, 1) from default_rng(seed) (the per-request
     states a serving cache holds, addressed by slot)."""

@@ -59,6 +59,30 @@ def test_decode_step(dtype, d, n):
     _check(x, out.float().cpu().numpy().astype(np.float64), state.cpu().numpy().astype(np.float64), tol)
 
 
+def test_decode_step_state_past_4gib():
+    """2,048 sequences x 32 V heads x 128 x 128 fp32 = 4 GiB of state, so the last sequences'
+    states start past byte offset 2^32; sampled sequences from both ends are checked against the
+    oracle."""
+    import linear_attention_sequence_02_amd as gdn
+    n = 2048
+    x = I.draw(lengths=[1] * n, hqk=16, hv=32, dk=128, dtype="bf16", seed=1010, name="decode_bf16_N2048")
+    s0 = I.large_state(n, 32, 128, seed=1011)
+    dev = to_device(x)
+    state = torch.from_numpy(s0).cuda()
+    log(f"[gpu] gdn_decode_step {x.name} state {state.numel() * 4 / 2**30:.1f} GiB")
+    out = gdn.gdn_decode_step(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], state, scale=x.scale)
+    torch.cuda.synchronize()
+    pick = [0, 1, 1023, 1024, 2046, 2047]
+    ref_o, ref_f = oracle.recurrent(x.q[pick], x.k[pick], x.v[pick], x.g[pick], x.beta[pick], s0[pick],
+                                    np.arange(len(pick) + 1, dtype=np.int32), scale=x.scale)
+    idx = torch.tensor(pick, device="cuda")
+    got_o = out.index_select(0, idx).float().cpu().numpy().astype(np.float64)
+    got_f = state.index_select(0, idx).cpu().numpy().astype(np.float64)
+    eo, ef = rel_l2(got_o, ref_o), rel_l2(got_f, ref_f)
+    log(f"[parity] {x.name} sequences {pick}: out rel={eo:.3e} state rel={ef:.3e}")
+    assert eo <= TOL_BF16 and ef <= TOL_BF16
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_decode_group3(dtype):
     """d = 128 decode with three V heads sharing one QK head, 5 sequences (an odd head count
