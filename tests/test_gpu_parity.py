@@ -148,6 +148,34 @@ def test_prefill_bf16_thousand_tiny_sequences():
     _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
 
 
+def test_prefill_states_past_4gib():
+    """2,048 sequences (mostly one token; the last two 130 and 64 tokens) with 4 GiB of initial and
+    4 GiB of final states: the far sequences' states sit past byte offset 2^32. Sampled sequences
+    from both ends against the oracle."""
+    import linear_attention_sequence_02_amd as gdn
+    n = 2048
+    lengths = [1] * n
+    lengths[0], lengths[-2], lengths[-1] = 70, 130, 64
+    x = I.draw(lengths=lengths, hqk=16, hv=32, dk=128, dtype="bf16", seed=1012, name="prefill_bf16_N2048")
+    s0 = I.large_state(n, 32, 128, seed=1013)
+    dev = to_device(x)
+    log(f"[gpu] gdn_prefill {x.name} T={x.T} initial and final states 4.0 GiB each")
+    out, fin = gdn.gdn_prefill(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], torch.from_numpy(s0).cuda(),
+                               dev["cu"], scale=x.scale)
+    torch.cuda.synchronize()
+    cu = x.cu_seqlens
+    pick = [0, 1, 1024, 2046, 2047]
+    rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in pick])
+    sub_cu = np.concatenate([[0], np.cumsum([cu[i + 1] - cu[i] for i in pick])]).astype(np.int32)
+    ref_o, ref_f = oracle.recurrent(x.q[rows], x.k[rows], x.v[rows], x.g[rows], x.beta[rows], s0[pick], sub_cu,
+                                    scale=x.scale)
+    got_o = out.index_select(0, torch.from_numpy(rows).cuda()).float().cpu().numpy().astype(np.float64)
+    got_f = fin.index_select(0, torch.tensor(pick, device="cuda")).cpu().numpy().astype(np.float64)
+    eo, ef = rel_l2(got_o, ref_o), rel_l2(got_f, ref_f)
+    log(f"[parity] {x.name} sequences {pick}: out rel={eo:.3e} state rel={ef:.3e}")
+    assert eo <= TOL_BF16 and ef <= TOL_BF16
+
+
 def test_prefill_bf16_qwen_layer_T4096():
     x = I.qwen3_next_prefill(T=4096)
     out, fin = run_prefill(x)
