@@ -24,6 +24,8 @@ Roofline figures use algorithmic work only:
   multi-token decode ("decode_multi"): 4 tokens per sequence from one state,
       256 sequences: the state read and written once plus 4 tokens' inputs and
       outputs, 1,099,169,792 bytes per step
+  short prefill ("prefill_graph_replay"): the T = 4096 layer, eager calls against
+      replays of a graph holding 16 calls, wall clock per step
   backward ("backward"): gradients of the prefill on the T = 4096 layer shape,
       against the fp32 peak (157.3 TFLOP/s) at 17 d^2 flop per token and V head
       (the recomputation of forward states not counted), over its four kernels
@@ -420,6 +422,23 @@ def main():
                                                "traffic": recorded_traffic("gdn_decode_multi", ym.name)}}
         log(f"[bench] multi-token decode {mms:.3f} ms/step, {mgbs:.1f} GB/s")
         del dm, stm, om
+
+    # Launch overhead of a short prefill (the 4,096-token layer: three launches of ~0.04 ms and the
+    # combine), eager calls against replays of a captured graph.
+    x4 = I.qwen3_next_prefill(T=4096)
+    d4 = to_device(x4, dev)
+    o4 = torch.empty_like(d4["v"])
+    f4 = torch.empty((1, x4.hv, x4.dv, x4.dk), dtype=torch.float32, device=dev)
+    ws4 = torch.empty(max(1, gdn.gdn_prefill_workspace_size(x4.T, 1, x4.hqk, x4.hv, x4.dk, x4.dv, gdn.GDN_BF16)),
+                      dtype=torch.uint8, device=dev)
+
+    def prefill4():
+        gdn.gdn_prefill(d4["q"], d4["k"], d4["v"], d4["g"], d4["beta"], out=o4, final_state=f4, workspace=ws4)
+
+    result["prefill_graph_replay"] = {"workload": "qwen3next_gdn_prefill_T4096",
+                                      **graph_vs_eager(prefill4, args.steps, torch)}
+    log(f"[bench] prefill T=4096 graph replay {result['prefill_graph_replay']}")
+    del d4, o4, f4, ws4
 
     if not args.no_backward:
         # Backward of the prefill on the 4,096-token Qwen3-Next layer shape (bf16 inputs, fp32 gradients).
