@@ -32,8 +32,9 @@ Roofline figures use algorithmic work only:
   with q and k L2-normalised in the kernels ("prefill_qk_l2norm",
       "decode.qk_l2norm"): the same inputs and algorithmic work
 Peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8.0 TB/s.
-"step_ms" gives the mean, median and min of the prefill step (a further pass
-with events around each call). The timed run behind `value` has no
+"step_ms" gives the mean, median and min of the prefill step over a further pass
+with events around each call (so its mean can differ from "ms_per_step", the
+timed run's). The timed run behind `value` has no
 per-kernel instrumentation; the per-kernel launch times come from a separate
 run of the same number of steps. "parity" is the rel-L2 (fp64) of the timed
 run's output, and of its final state when the oracle sample covers the
@@ -236,8 +237,8 @@ def rel_l2(a, ref):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--T", type=int, default=65536)
     ap.add_argument("--decode-seqs", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -306,7 +307,7 @@ def main():
                      "traffic": recorded_traffic(dom, workload), "ms_per_launch": dom_ms,
                      "tokens_per_launch": out_tokens, "flop_per_launch": PREFILL_FLOP_PER_TOKEN * out_tokens,
                      "longest_launch": by_time, "segment_chunks": seg_chunks},
-        "step_ms": {"mean": ms, "median": float(np.median(each)), "min": float(np.min(each)),
+        "step_ms": {"mean": float(np.mean(each)), "median": float(np.median(each)), "min": float(np.min(each)),
                     "n": len(each)},
         "prefill_path": {"tflops_algorithmic": path_tflops, "frac_mfma_peak": path_tflops / PEAK_BF16_TFLOPS,
                          "gbs_algorithmic": path_gbs, "frac_hbm_peak": path_gbs / PEAK_HBM_GBS,
