@@ -121,6 +121,14 @@ def test_prefill_fp32_qwen_shape():
     _check(x, out, fin, TOL_FP32)
 
 
+def test_prefill_fp32_long_layer():
+    # 16,384 tokens on the layer's head shape in the fp32 mode: 256 chunks of accumulated state,
+    # still held to the 1e-4 bar.
+    x = I.qwen3_next_prefill(T=16384, dtype="fp32", seed=72)
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_FP32)
+
+
 # ---------------------------------------------------------------- bf16 MFMA prefill
 
 def test_prefill_bf16_small_varlen():
