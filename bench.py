@@ -13,10 +13,17 @@ Roofline figures use algorithmic work only:
       segment-parallel in three launches: the first produces the outputs of
       each sequence's first segment and the maps of the other segments, a
       combine, and the output pass for segments 1 onward. The roofline object
-      is the output pass ("gdn_segment_out"), priced at 4,194,304 flop per
-      token it produces (all tokens but the first segment's, whose length
-      comes from gdn_prefill_segment_chunks); the map pass and the combine are
-      extra work of the schedule and count only in "prefill_path".
+      is the whole call: 4,194,304 flop per token of the T = 65536 input over
+      the sum of the three launches' mean durations (the map pass and the
+      combine are extra work of the schedule, so they count against it). Its
+      "output_pass" entry prices the last launch alone on the tokens it
+      produces (all but each sequence's first segment, whose length comes from
+      gdn_prefill_segment_chunks).
+  configs ("configs"): the same record for the 4,096-token layer, the
+      8-sequence varlen batch and the 262,144-token long context, each with
+      tokens/s, the whole-call MFMA fraction and the longest launch's own
+      fraction over the tokens it produces. They run before the headline
+      workload.
   decode: 1,080,098,816 bytes per step for 256 sequences (state read + write
       plus q, k, v, g, beta, out); also on a state pool addressed by slot
       ("decode.slots"), and as eager calls against graph replays, wall clock
@@ -27,8 +34,9 @@ Roofline figures use algorithmic work only:
   short prefill ("prefill_graph_replay"): the T = 4096 layer, eager calls against
       replays of a graph holding 16 calls, wall clock per step
   backward ("backward"): gradients of the prefill on the T = 4096 layer shape,
-      against the fp32 peak (157.3 TFLOP/s) at 17 d^2 flop per token and V head
-      (the recomputation of forward states not counted), over its four kernels
+      on fp32 MFMA, against the fp32 matrix peak (157.3 TFLOP/s) at 17 d^2 flop
+      per token and V head (the recomputation of forward states not counted),
+      over its four kernels
   with q and k L2-normalised in the kernels ("prefill_qk_l2norm",
       "decode.qk_l2norm"): the same inputs and algorithmic work
 Peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8.0 TB/s.
@@ -66,7 +74,7 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
 PREFILL_FLOP_PER_TOKEN = 4_194_304
 PREFILL_BYTES_PER_TOKEN = 24_832
-PEAK_FP32_VECTOR_TFLOPS = 157.3
+PEAK_FP32_MFMA_TFLOPS = 157.3
 # Backward, per token over all 32 V heads (d = 128): the reverse step's products with the state
 # (S k, dS update by do q^T, dS k, S^T do, dS^T u and S^T du, <dS, S>, the dS recurrence) at
 # 17 d^2 flop per V head; the recomputation of the forward states is the implementation's own.
@@ -234,6 +242,56 @@ def rel_l2(a, ref):
     return float(np.linalg.norm((a - ref).ravel()) / np.linalg.norm(ref.ravel()))
 
 
+def launch_tokens(x, seg_chunks):
+    """Tokens whose outputs each launch of the segment schedule produces: each sequence's first
+    segment in the map launch ("gdn_segment_maps", or "gdn_segment_out" when no sequence spans a
+    second segment), the rest in the output launch."""
+    lens = np.diff(x.cu_seqlens.astype(np.int64))
+    first = np.minimum(lens, 64 * seg_chunks)
+    multi = x.num_seqs > 1 or x.T > 64 * seg_chunks
+    if not multi:
+        return {"gdn_segment_out": int(x.T)}
+    return {"gdn_segment_maps": int(first.sum()), "gdn_segment_out": int((lens - first).sum())}
+
+
+def prefill_record(gdn, torch, x, dev, steps, warmup, per_step=None):
+    """Time gdn_prefill on one input set (resident in HBM, workspace preallocated): tokens/s of the
+    whole call, its MFMA fraction (algorithmic flop over the sum of the launches' mean durations),
+    and the longest launch's own fraction over the tokens whose outputs it produces."""
+    d = to_device(x, dev)
+    out = torch.empty_like(d["v"])
+    fin = torch.empty((x.num_seqs, x.hv, x.dv, x.dk), dtype=torch.float32, device=dev)
+    ws_bytes = gdn.gdn_prefill_workspace_size(x.T, x.num_seqs, x.hqk, x.hv, x.dk, x.dv, gdn.GDN_BF16)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+    cu = d["cu"] if x.num_seqs > 1 else None
+
+    def call():
+        gdn.gdn_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], cu, out=out, final_state=fin,
+                        workspace=ws)
+
+    ms, kern = time_calls(call, steps, warmup, torch, per_step=per_step)
+    seg_chunks = gdn.gdn_prefill_segment_chunks(x.T, x.num_seqs, x.hqk, x.hv, x.dk, x.dv, gdn.GDN_BF16)
+    per_launch = {k_: v_[1] for k_, v_ in kern.items()}
+    call_ms = sum(per_launch.values()) if per_launch else ms
+    flop = PREFILL_FLOP_PER_TOKEN * x.T
+    tokens = launch_tokens(x, seg_chunks)
+    longest = max(per_launch, key=per_launch.get) if per_launch else None
+    rec = {
+        "workload": x.name, "tokens": x.T, "num_seqs": x.num_seqs, "ms_per_step": ms, "steps": steps,
+        "warmup": warmup, "tokens_per_s": x.T / (ms / 1e3),
+        "frac_mfma_peak_whole_call": flop / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "frac_hbm_peak_whole_call": PREFILL_BYTES_PER_TOKEN * x.T / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        "kernels_ms_per_launch": per_launch, "launches_ms_sum": call_ms, "segment_chunks": seg_chunks,
+        "tokens_per_launch": tokens,
+    }
+    if longest is not None:
+        lt = tokens.get(longest, 0)
+        rec["longest_launch"] = {"kernel": longest, "ms_per_launch": per_launch[longest], "tokens": lt,
+                                 "frac_mfma_peak": PREFILL_FLOP_PER_TOKEN * lt / (per_launch[longest] / 1e3) / 1e12
+                                 / PEAK_BF16_TFLOPS}
+    return rec, (d, out, fin, ws, call)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +302,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the T=4096, varlen and T=262144 records")
+    ap.add_argument("--config", default=None,
+                    help="time only this prefill configuration and print its record (for profiling): one of "
+                         "qwen3next_gdn_prefill_T4096, qwen3next_gdn_varlen8, qwen3next_gdn_long_T262144")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one 256 MiB device-to-device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -259,32 +321,57 @@ def main():
     from synth import inputs as I
 
     dev = torch.device("cuda:0")
+
+    # The other prefill configurations first (their own inputs, freed afterwards): the 4,096-token
+    # layer, the 8-sequence varlen batch with initial states, and the 262,144-token long context.
+    configs = {}
+    table = (("qwen3next_gdn_prefill_T4096", lambda: I.qwen3_next_prefill(T=4096), args.steps),
+             ("qwen3next_gdn_varlen8", I.varlen_prefill, args.steps),
+             ("qwen3next_gdn_long_T262144", I.long_context, max(3, args.steps // 4)))
+    if args.config is not None:
+        table = tuple(t_ for t_ in table if t_[0] == args.config)
+        if not table:
+            print(f"unknown --config {args.config}", file=sys.stderr)
+            sys.exit(2)
+    if not args.no_configs:
+        for name, make, steps in table:
+            log(f"[bench] config {name}: generating inputs")
+            xc = make()
+            rec, keep = prefill_record(gdn, torch, xc, dev, steps, max(2, args.warmup // 4))
+            if name == "qwen3next_gdn_varlen8":
+                rec["lengths"] = xc.meta["lengths"]
+            if name == "qwen3next_gdn_long_T262144":
+                rec["mean_alpha"] = xc.meta["mean_alpha"]
+            configs[name] = rec
+            log(f"[bench] config {name}: {rec['ms_per_step']:.3f} ms/step, {rec['tokens_per_s']:.3e} tokens/s, "
+                f"whole call {rec['frac_mfma_peak_whole_call']:.3f} of bf16 peak")
+            del keep, xc
+            torch.cuda.empty_cache()
+    if args.config is not None:
+        print(json.dumps({"config": args.config, **configs[args.config]}), flush=True)
+        return
+
     log(f"[bench] generating T={args.T} inputs")
     x = I.qwen3_next_prefill(T=args.T)
-    d = to_device(x, dev)
-    out = torch.empty_like(d["v"])
-    fin = torch.empty((1, x.hv, x.dv, x.dk), dtype=torch.float32, device=dev)
-    ws_bytes = gdn.gdn_prefill_workspace_size(x.T, 1, x.hqk, x.hv, x.dk, x.dv, gdn.GDN_BF16)
-    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
-
-    def prefill():
-        gdn.gdn_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, None, out=out, final_state=fin,
-                        workspace=ws)
-
     log(f"[bench] prefill: {args.warmup} warmup + {args.steps} timed steps")
     each = []
-    ms, kern = time_calls(prefill, args.steps, args.warmup, torch, per_step=each)
+    rec, (d, out, fin, ws, prefill) = prefill_record(gdn, torch, x, dev, args.steps, args.warmup, per_step=each)
+    ms = rec["ms_per_step"]
+    kern = rec["kernels_ms_per_launch"]
     tokens_per_s = x.T / (ms / 1e3)
-    by_time = max(kern, key=lambda k_: kern[k_][0] * kern[k_][1]) if kern else None
-    seg_chunks = gdn.gdn_prefill_segment_chunks(x.T, 1, x.hqk, x.hv, x.dk, x.dv, gdn.GDN_BF16)
-    out_tokens = x.T - min(x.T, 64 * seg_chunks) if "gdn_segment_maps" in kern else x.T
+    seg_chunks = rec["segment_chunks"]
+    out_tokens = rec["tokens_per_launch"].get("gdn_segment_out", 0)
+    call_ms = rec["launches_ms_sum"]
+    call_tflops = PREFILL_FLOP_PER_TOKEN * x.T / (call_ms / 1e3) / 1e12
     dom = "gdn_segment_out"
-    dom_ms = kern[dom][1] if dom in kern else float("nan")
+    dom_ms = kern.get(dom, float("nan"))
     dom_tflops = PREFILL_FLOP_PER_TOKEN * out_tokens / (dom_ms / 1e3) / 1e12
     path_tflops = PREFILL_FLOP_PER_TOKEN * x.T / (ms / 1e3) / 1e12
     path_gbs = PREFILL_BYTES_PER_TOKEN * x.T / (ms / 1e3) / 1e9
     workload = f"qwen3next_gdn_prefill_T{x.T}"
     log(f"[bench] prefill {ms:.3f} ms/step, {tokens_per_s:.3e} tokens/s; kernels {kern}")
+    traffic = [recorded_traffic(k_, workload) for k_ in kern]
+    call_traffic = sum(traffic) if traffic and all(t_ is not None for t_ in traffic) else None
 
     result = {
         "metric": METRIC,
@@ -302,16 +389,21 @@ def main():
         "config": {"workload": workload, "batch": 1, "seq_len": x.T,
                    "num_qk_heads": x.hqk, "num_v_heads": x.hv, "head_dim": x.dk, "chunk": 64,
                    "seed": x.seed, "initial_state": "zeros"},
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": dom_tflops,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": recorded_traffic(dom, workload), "ms_per_launch": dom_ms,
-                     "tokens_per_launch": out_tokens, "flop_per_launch": PREFILL_FLOP_PER_TOKEN * out_tokens,
-                     "longest_launch": by_time, "segment_chunks": seg_chunks},
+        "roofline": {"kernel": "+".join(kern), "bound": "mfma", "achieved": call_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": call_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": call_traffic, "ms_per_call": call_ms, "tokens_per_call": x.T,
+                     "flop_per_call": PREFILL_FLOP_PER_TOKEN * x.T, "segment_chunks": seg_chunks,
+                     "target_frac": 0.40,
+                     "output_pass": {"kernel": dom, "achieved": dom_tflops, "frac": dom_tflops / PEAK_BF16_TFLOPS,
+                                     "ms_per_launch": dom_ms, "tokens_per_launch": out_tokens,
+                                     "flop_per_launch": PREFILL_FLOP_PER_TOKEN * out_tokens,
+                                     "traffic": recorded_traffic(dom, workload)}},
         "step_ms": {"mean": float(np.mean(each)), "median": float(np.median(each)), "min": float(np.min(each)),
                     "n": len(each)},
         "prefill_path": {"tflops_algorithmic": path_tflops, "frac_mfma_peak": path_tflops / PEAK_BF16_TFLOPS,
                          "gbs_algorithmic": path_gbs, "frac_hbm_peak": path_gbs / PEAK_HBM_GBS,
-                         "kernels_ms_per_launch": {k_: v_[1] for k_, v_ in kern.items()}},
+                         "kernels_ms_per_launch": kern},
+        "configs": configs,
     }
     out_host = out.view(torch.int16).cpu().numpy()
     fin_host = fin.cpu().numpy()
@@ -461,10 +553,10 @@ def main():
         btf = BACKWARD_FLOP_PER_TOKEN * xb.T / (bkms / 1e3) / 1e12
         result["backward"] = {"workload": "qwen3next_gdn_backward_T4096", "steps": bsteps, "ms_per_step": bms,
                               "kernel_ms_per_launch": bparts, "tokens_per_s": xb.T / (bms / 1e3),
-                              "roofline": {"kernel": "gdn_backward_prep+scan+grad+sums", "bound": "alu",
+                              "roofline": {"kernel": "gdn_backward_prep+scan+grad+sums", "bound": "mfma",
                                            "achieved": btf,
-                                           "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
-                                           "frac": btf / PEAK_FP32_VECTOR_TFLOPS}}
+                                           "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                                           "frac": btf / PEAK_FP32_MFMA_TFLOPS}}
         log(f"[bench] backward {bms:.3f} ms/step")
         del db, gout, wsb
 

@@ -140,10 +140,39 @@ def _check(t, name, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _expect(t, name, shape):
+    """Raise ValueError unless t is None or has `shape` (None entries match any size)."""
+    if t is None:
+        return
+    if t.dim() != len(shape) or any(e is not None and int(a) != int(e) for a, e in zip(t.shape, shape)):
+        want = "[" + ", ".join("*" if e is None else str(int(e)) for e in shape) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+
+
+def _token_shapes(q, k, v, g, beta, out=None, out_name="out"):
+    """Shapes shared by every entry point: q, k [T, Hqk, dk], v and out [T, Hv, dv], g, beta [T, Hv]."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError(f"q and v must be 3-D [tokens, heads, dim], got {list(q.shape)} and {list(v.shape)}")
+    T, hqk, dk = q.shape
+    hv, dv = v.shape[1], v.shape[2]
+    _expect(k, "k", (T, hqk, dk))
+    _expect(v, "v", (T, hv, dv))
+    _expect(g, "g", (T, hv))
+    _expect(beta, "beta", (T, hv))
+    _expect(out, out_name, (T, hv, dv))
+    return T, hqk, dk, hv, dv
+
+
 def _stream(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _seq_count(cu_seqlens) -> int:
+    if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+        raise ValueError(f"cu_seqlens must be 1-D [N + 1], got shape {list(cu_seqlens.shape)}")
+    return cu_seqlens.shape[0] - 1
 
 
 def gdn_prefill_workspace_size(total_tokens: int, num_seqs: int, num_qk_heads: int, num_v_heads: int,
@@ -175,9 +204,10 @@ def gdn_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, scale:
     for name, t in (("g", g), ("beta", beta), ("initial_state", initial_state)):
         _check(t, name, torch.float32, dev)
     _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
-    T, hqk, dk = q.shape
-    hv, dv = v.shape[1], v.shape[2]
-    n = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    T, hqk, dk, hv, dv = _token_shapes(q, k, v, g, beta, out)
+    n = 1 if cu_seqlens is None else _seq_count(cu_seqlens)
+    _expect(initial_state, "initial_state", (n, hv, dv, dk))
+    _expect(final_state, "final_state", (n, hv, dv, dk))
     if out is None:
         out = torch.empty((T, hv, dv), dtype=q.dtype, device=dev)
     _check(out, "out", q.dtype, dev)
@@ -205,8 +235,8 @@ def gdn_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, out=None, st
         _check(t, name, q.dtype, dev)
     for name, t in (("g", g), ("beta", beta), ("state", state)):
         _check(t, name, torch.float32, dev)
-    N, hqk, dk = q.shape
-    hv, dv = v.shape[1], v.shape[2]
+    N, hqk, dk, hv, dv = _token_shapes(q, k, v, g, beta, out)
+    _expect(state, "state", (N, hv, dv, dk))
     if out is None:
         out = torch.empty((N, hv, dv), dtype=q.dtype, device=dev)
     _check(out, "out", q.dtype, dev)
@@ -230,8 +260,9 @@ def gdn_decode_step_slots(q, k, v, g, beta, state_pool, state_indices, *, scale:
     for name, t in (("g", g), ("beta", beta), ("state_pool", state_pool)):
         _check(t, name, torch.float32, dev)
     _check(state_indices, "state_indices", torch.int32, dev)
-    N, hqk, dk = q.shape
-    hv, dv = v.shape[1], v.shape[2]
+    N, hqk, dk, hv, dv = _token_shapes(q, k, v, g, beta, out)
+    _expect(state_pool, "state_pool", (None, hv, dv, dk))
+    _expect(state_indices, "state_indices", (N,))
     if out is None:
         out = torch.empty((N, hv, dv), dtype=q.dtype, device=dev)
     _check(out, "out", q.dtype, dev)
@@ -258,9 +289,11 @@ def gdn_prefill_slots(q, k, v, g, beta, state_pool, state_indices, has_initial_s
     for name, t in (("state_indices", state_indices), ("has_initial_state", has_initial_state),
                     ("cu_seqlens", cu_seqlens)):
         _check(t, name, torch.int32, dev)
-    T, hqk, dk = q.shape
-    hv, dv = v.shape[1], v.shape[2]
-    n = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    T, hqk, dk, hv, dv = _token_shapes(q, k, v, g, beta, out)
+    n = 1 if cu_seqlens is None else _seq_count(cu_seqlens)
+    _expect(state_pool, "state_pool", (None, hv, dv, dk))
+    _expect(state_indices, "state_indices", (n,))
+    _expect(has_initial_state, "has_initial_state", (n,))
     if out is None:
         out = torch.empty((T, hv, dv), dtype=q.dtype, device=dev)
     _check(out, "out", q.dtype, dev)
@@ -292,11 +325,13 @@ def gdn_decode_multi(q, k, v, g, beta, state, num_tokens: int, *, state_indices=
     for name, t in (("g", g), ("beta", beta), ("state", state)):
         _check(t, name, torch.float32, dev)
     _check(state_indices, "state_indices", torch.int32, dev)
-    rows, hqk, dk = q.shape
-    hv, dv = v.shape[1], v.shape[2]
+    rows, hqk, dk, hv, dv = _token_shapes(q, k, v, g, beta, out)
     if num_tokens < 1 or rows % num_tokens:
         raise ValueError(f"{rows} token rows are not a whole number of sequences of {num_tokens} tokens")
     N = rows // num_tokens
+    _expect(state, "state", (None if state_indices is not None else N, hv, dv, dk))
+    _expect(state_indices, "state_indices", (N,))
+    _expect(token_states if isinstance(token_states, torch.Tensor) else None, "token_states", (rows, hv, dv, dk))
     if out is None:
         out = torch.empty((rows, hv, dv), dtype=q.dtype, device=dev)
     _check(out, "out", q.dtype, dev)
@@ -330,11 +365,19 @@ def gdn_prefill_ex(q, k, v, g, beta, initial_state=None, final_state=None, state
     for name, t in (("state_indices", state_indices), ("has_initial_state", has_initial_state),
                     ("cu_seqlens", cu_seqlens)):
         _check(t, name, torch.int32, dev)
-    T, hqk, dk = q.shape
-    hv, dv = v.shape[1], v.shape[2]
-    n = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    T, hqk, dk, hv, dv = _token_shapes(q, k, v, g, beta, out)
+    n = 1 if cu_seqlens is None else _seq_count(cu_seqlens)
     num_slots = 0
+    rows = None if state_indices is not None else n
+    _expect(initial_state, "initial_state", (rows, hv, dv, dk))
+    _expect(final_state, "final_state", (rows, hv, dv, dk))
+    _expect(state_indices, "state_indices", (n,))
+    _expect(has_initial_state, "has_initial_state", (n,))
     if state_indices is not None:
+        if (initial_state is not None and final_state is not None
+                and initial_state.shape[0] != final_state.shape[0]):
+            raise ValueError(f"initial_state and final_state pools differ in size ({initial_state.shape[0]} "
+                             f"and {final_state.shape[0]} slots); slot indices address both")
         pool = initial_state if initial_state is not None else final_state
         num_slots = 0 if pool is None else pool.shape[0]
     if out is None:
@@ -365,10 +408,13 @@ def gdn_decode_ex(q, k, v, g, beta, state, *, num_tokens: int = 1, state_indices
     for name, t in (("g", g), ("beta", beta), ("state", state)):
         _check(t, name, torch.float32, dev)
     _check(state_indices, "state_indices", torch.int32, dev)
-    rows, hqk, dk = q.shape
-    hv, dv = v.shape[1], v.shape[2]
+    rows, hqk, dk, hv, dv = _token_shapes(q, k, v, g, beta, out)
     if num_tokens < 1 or rows % num_tokens:
         raise ValueError(f"{rows} token rows are not a whole number of sequences of {num_tokens} tokens")
+    N = rows // num_tokens
+    _expect(state, "state", (None if state_indices is not None else N, hv, dv, dk))
+    _expect(state_indices, "state_indices", (N,))
+    _expect(token_states if isinstance(token_states, torch.Tensor) else None, "token_states", (rows, hv, dv, dk))
     if out is None:
         out = torch.empty((rows, hv, dv), dtype=q.dtype, device=dev)
     _check(out, "out", q.dtype, dev)
@@ -405,9 +451,10 @@ def gdn_backward(q, k, v, g, beta, d_out, initial_state=None, cu_seqlens=None, d
     for name, t in (("g", g), ("beta", beta), ("initial_state", initial_state), ("d_final_state", d_final_state)):
         _check(t, name, torch.float32, dev)
     _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
-    T, hqk, dk = q.shape
-    hv, dv = v.shape[1], v.shape[2]
-    n = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    T, hqk, dk, hv, dv = _token_shapes(q, k, v, g, beta, d_out, "d_out")
+    n = 1 if cu_seqlens is None else _seq_count(cu_seqlens)
+    _expect(initial_state, "initial_state", (n, hv, dv, dk))
+    _expect(d_final_state, "d_final_state", (n, hv, dv, dk))
     f32 = dict(dtype=torch.float32, device=dev)
     res = {"dq": torch.empty((T, hqk, dk), **f32), "dk": torch.empty((T, hqk, dk), **f32),
            "dv": torch.empty((T, hv, dv), **f32), "dg": torch.empty((T, hv), **f32),

@@ -904,14 +904,12 @@ int64_t num_segments(int64_t total_tokens, int32_t num_seqs, int L) {
 // CUs / Hv segments per sequence, with enough chunks per segment to amortise
 // the map work (at least 8).
 int cp_segment_chunks(int64_t total_tokens, int32_t num_seqs, int32_t num_v_heads) {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, c = 0;
-        if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
-            cus = c;
-        else
-            cus = 256;
-    }
+    // The compute-unit count of the current device, looked up on every call (the runtime answers
+    // from its own per-device table), so that each device gets its own segment length.
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
     const int64_t chunks = (total_tokens + kChunk - 1) / kChunk;
     const int64_t per_head = cus / num_v_heads > 1 ? cus / num_v_heads : 1;
     int64_t L = (chunks + per_head + num_seqs - 1) / (per_head + num_seqs);

@@ -166,6 +166,7 @@ def draw(
     fixed_g: float | None = None,
     fixed_beta: float | None = None,
     qk_unit: bool = True,
+    k_spread: float | None = None,
 ) -> GdnInputs:
     """Draw one seeded input set.
 
@@ -178,6 +179,10 @@ def draw(
     fixed_g / fixed_beta replace the drawn values by a constant (used by
     the special cases whose closed forms the tests check). qk_unit=False
     leaves q and k unnormalised (for the in-kernel normalisation mode).
+    k_spread, when given, makes the keys of each QK head nearly parallel:
+    k = unit(b_h + k_spread * n_t) with one N(0, 1) direction b_h per QK head
+    (child generator [seed, 4, 0]) and n_t the usual key noise, so that the
+    decay-masked key Gram of a chunk is close to all ones.
     """
     if dtype not in ("bf16", "fp32"):
         raise ValueError(dtype)
@@ -196,7 +201,15 @@ def draw(
 
     rows = _unit_rows if qk_unit else _scaled_rows
     q = rows(seed, 1, (T, hqk, dk))
-    k = rows(seed, 2, (T, hqk, dk))
+    if k_spread is None:
+        k = rows(seed, 2, (T, hqk, dk))
+    else:
+        base = _block_rng(seed, 4, 0).standard_normal((hqk, dk))
+
+        def near(b, shp):
+            x = base[None] + k_spread * _block_rng(seed, 2, b).standard_normal(shp, dtype=np.float32).astype(np.float64)
+            return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        k = _fill_blocks((T, hqk, dk), near)
     v = _normal_rows(seed, 3, (T, hv, dv))
     g = (-_softplus(rng.standard_normal((T, hv)) + g_mean)).astype(np.float32)
     beta = _sigmoid(rng.standard_normal((T, hv))).astype(np.float32)
@@ -215,6 +228,7 @@ def draw(
         "g_mean_param": g_mean,
         "s0_std": s0_std,
         "mean_alpha": float(np.mean(np.exp(g.astype(np.float64)))) if T else None,
+        "k_spread": k_spread,
     }
     return GdnInputs(q=q, k=k, v=v, g=g, beta=beta, s0=s0, cu_seqlens=cu, dtype=dtype,
                      scale=float(scale), name=name, seed=seed, meta=meta)

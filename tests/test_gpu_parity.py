@@ -19,7 +19,9 @@ pytestmark = pytest.mark.gpu
 
 TOL_BF16 = 1e-2
 TOL_FP32 = 1e-4
-TOL_BF16_SLICE = 2e-2   # worst single (sequence, head) slice; the bar itself is on the whole tensor
+# The worst single (sequence, V head) slice is held to the same bar as the whole tensor, so that an
+# error confined to one short sequence or one head cannot hide in the global norm.
+TOL_BF16_SLICE = TOL_BF16
 
 
 def _oracle(x, heads=None):
@@ -204,13 +206,78 @@ def test_prefill_bf16_varlen8():
     _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
 
 
-def test_prefill_bf16_long_context_sampled_heads():
-    # T = 262144 in the launch configuration of the full layer; the oracle
-    # recomputes one QK head's two V heads (heads are independent).
+def _check_by_head_groups(x, out, fin, tol, group=16):
+    """Whole-tensor and per-(sequence, V head) rel-L2 of device results against the oracle, run on
+    `group` V heads at a time: the sums of squared differences and of squared reference values are
+    accumulated over the groups, so the whole-tensor figure is exact without holding the fp64
+    reference of every head at once."""
+    num_o = den_o = num_f = den_f = 0.0
+    worst_o = worst_f = 0.0
+    cu = x.cu_seqlens
+    for h0 in range(0, x.hv, group):
+        h1 = min(x.hv, h0 + group)
+        log(f"[oracle] {x.name}: V heads {h0}..{h1 - 1}")
+        ref_o, ref_f = _oracle(x, heads=(h0, h1))
+        got_o = out[:, h0:h1].float().cpu().numpy().astype(np.float64)
+        got_f = fin[:, h0:h1].cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got_o)) and np.all(np.isfinite(got_f))
+        do = got_o - ref_o
+        df = got_f - ref_f
+        num_o += float(np.sum(do * do))
+        den_o += float(np.sum(ref_o * ref_o))
+        num_f += float(np.sum(df * df))
+        den_f += float(np.sum(ref_f * ref_f))
+        worst_o = max(worst_o, per_seq_head_rel(got_o, ref_o, cu))
+        worst_f = max(worst_f, per_state_rel(got_f, ref_f))
+        del ref_o, ref_f, got_o, got_f, do, df
+    eo, ef = math.sqrt(num_o / den_o), math.sqrt(num_f / den_f)
+    log(f"[parity] {x.name}: out rel={eo:.3e} (worst slice {worst_o:.3e})  state rel={ef:.3e} "
+        f"(worst {worst_f:.3e})")
+    assert eo <= tol and ef <= tol
+    assert worst_o <= TOL_BF16_SLICE and worst_f <= TOL_BF16_SLICE
+
+
+def _run_prefill_device(x):
+    import linear_attention_sequence_02_amd as gdn
+    d = to_device(x)
+    log(f"[gpu] gdn_prefill {x.name} T={x.T} N={x.num_seqs} Hqk={x.hqk} Hv={x.hv} d={x.dk} {x.dtype}")
+    out, fin = gdn.gdn_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d["cu"], scale=x.scale)
+    torch.cuda.synchronize()
+    del d
+    return out, fin
+
+
+def test_prefill_bf16_long_context():
+    # T = 262144 in the launch configuration of the full layer, compared with the oracle on every
+    # V head (in two groups of 16 heads).
     x = I.long_context()
     log(f"[case] long context mean alpha={x.meta['mean_alpha']:.4f}")
+    out, fin = _run_prefill_device(x)
+    _check_by_head_groups(x, out, fin, TOL_BF16)
+
+
+def test_prefill_bf16_near_parallel_keys():
+    # The chunk solve near its worst conditioning: every key of a QK head within about 0.05 of one
+    # direction (the masked key Gram close to all ones), beta = 0.999 and alpha = exp(-1e-3), so
+    # (I + A) is close to the lower triangle of ones and each write nearly cancels the previous one.
+    # The layer's head shape at T = 4096 runs 8 segments of 8 chunks, so the segment maps and the
+    # combine see the same inputs.
+    x = I.draw(T=4096, hqk=16, hv=32, dk=128, dtype="bf16", seed=1020, k_spread=0.05, fixed_beta=0.999,
+               fixed_g=-1e-3, s0_std=0.1, name="bf16_near_parallel_keys_T4096")
     out, fin = run_prefill(x)
-    _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE, heads=(6, 8))
+    _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
+
+
+@pytest.mark.parametrize("g,beta", [(-1e-3, None), (-1e-4, 0.02)], ids=["g1e-3", "g1e-4_beta0.02"])
+def test_prefill_bf16_full_scale_carry(g, beta):
+    # The timed workload's launch configuration (T = 65536, 16/32 heads, 9 segments of 114 chunks)
+    # with slow decay and initial states, so the state carried across segment boundaries (the
+    # bf16-built segment maps composed by the combine) decides the result. With g = -1e-4 and
+    # beta = 0.02 the map of one segment keeps a norm of order 0.1.
+    x = I.draw(T=65536, hqk=16, hv=32, dk=128, dtype="bf16", seed=1021, fixed_g=g, fixed_beta=beta,
+               s0_std=0.5, name=f"bf16_carry_T65536_g{g:g}")
+    out, fin = _run_prefill_device(x)
+    _check_by_head_groups(x, out, fin, TOL_BF16, group=32)
 
 
 def test_prefill_bf16_scale_argument():
