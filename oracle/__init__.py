@@ -23,6 +23,9 @@ reading; the pages give none).
 
   backward(...)   fp64 gradients of the recurrence (backward.py: the rule written with
                   PyTorch CPU ops in float64, reversed by torch.autograd).
+  causal_conv1d(...), conv_prologue(...)
+                  the short causal convolution in front of the mixer and the input
+                  prologue built on it (conv.py: the definition written out in numpy).
   upcast(x)       exact fp64 value of a bf16-bit / fp32 / fp64 array.
   qk_normalize(x) that normalisation along the last axis, fp64.
 """
@@ -151,3 +154,4 @@ def rel_l2(x, ref) -> float:
 
 from .chunked import chunked  # noqa: E402,F401
 from .backward import backward  # noqa: E402,F401
+from .conv import causal_conv1d, conv_prologue, silu, split_heads  # noqa: E402,F401
