@@ -39,6 +39,12 @@ Roofline figures use algorithmic work only:
       over its four kernels
   with q and k L2-normalised in the kernels ("prefill_qk_l2norm",
       "decode.qk_l2norm"): the same inputs and algorithmic work
+  input prologue ("conv_prologue"): the short causal convolution (4 taps)
+      over the 8,192 q/k/v channels of the T = 65536 input with SiLU, the
+      q/k/v split and q/k L2 normalisation, against HBM at the bf16 input read
+      once and q, k, v written once (2 x 2 B per token and channel); and the
+      256-sequence decode step preceded by the prologue on one token each
+      ("decode_with_prologue", wall time of both launches)
 Peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8.0 TB/s.
 "step_ms" gives the mean, median and min of the prefill step over a further pass
 with events around each call (so its mean can differ from "ms_per_step", the
@@ -303,6 +309,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the T=4096, varlen and T=262144 records")
+    ap.add_argument("--no-conv", action="store_true", help="skip the input prologue records")
     ap.add_argument("--config", default=None,
                     help="time only this prefill configuration and print its record (for profiling): one of "
                          "qwen3next_gdn_prefill_T4096, qwen3next_gdn_varlen8, qwen3next_gdn_long_T262144")
@@ -515,6 +522,61 @@ def main():
                                                "traffic": recorded_traffic("gdn_decode_multi", ym.name)}}
         log(f"[bench] multi-token decode {mms:.3f} ms/step, {mgbs:.1f} GB/s")
         del dm, stm, om
+
+    if not args.no_conv:
+        # The input prologue (short causal convolution over the 8,192 q/k/v channels, SiLU, split, q/k
+        # L2 normalisation) over the T = 65536 layer input, HBM-bound: x read once, q/k/v written once.
+        T, hqk, hv, dd, K = args.T, 16, 32, 128, 4
+        C = (2 * hqk + hv) * dd
+        cx = I.conv_inputs(lengths=[T], hqk=hqk, hv=hv, d=dd, K=K, dtype="bf16", seed=1006, history=False,
+                           name=f"qwen3next_gdn_conv_prologue_T{T}")
+        xc = torch.from_numpy(cx.x).view(torch.bfloat16).to(dev)
+        wc = torch.from_numpy(cx.w).to(dev)
+        qc, kc_, vc = (torch.empty((T, hqk, dd), dtype=torch.bfloat16, device=dev),
+                       torch.empty((T, hqk, dd), dtype=torch.bfloat16, device=dev),
+                       torch.empty((T, hv, dd), dtype=torch.bfloat16, device=dev))
+        hc = torch.empty((1, K - 1, C), dtype=torch.bfloat16, device=dev)
+
+        def conv():
+            gdn.gdn_conv_prologue(xc, wc, None, None, num_qk_heads=hqk, num_v_heads=hv, silu=True, qk_l2norm=True,
+                                  q=qc, k=kc_, v=vc, conv_state_out=hc)
+
+        cms, ckern = time_calls(conv, args.steps, max(2, args.warmup // 4), torch)
+        cbytes = T * C * 2 * 2 + C * K * 4 + (K - 1) * C * 2
+        ckms = ckern.get("gdn_conv_prologue", (0, cms))[1]
+        cgbs = cbytes / (ckms / 1e3) / 1e9
+        result["conv_prologue"] = {"workload": cx.name, "kernel_size": K, "channels": C, "ms_per_step": cms,
+                                   "kernels_ms_per_launch": {k_: v_[1] for k_, v_ in ckern.items()},
+                                   "bytes_per_launch": cbytes, "tokens_per_s": T / (cms / 1e3),
+                                   "roofline": {"kernel": "gdn_conv_prologue", "bound": "hbm", "achieved": cgbs,
+                                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": cgbs / PEAK_HBM_GBS}}
+        log(f"[bench] conv prologue {cms:.3f} ms/step, {cgbs:.1f} GB/s")
+        del xc, wc, qc, kc_, vc, hc
+        # Decode with the prologue: 256 sequences, one token each, history and state carried in place.
+        n = args.decode_seqs
+        cd = I.conv_inputs(lengths=[1] * n, hqk=hqk, hv=hv, d=dd, K=K, dtype="bf16", seed=1007,
+                           name=f"qwen3next_gdn_conv_decode_N{n}")
+        yd = I.decode_batch(n)
+        dd_ = to_device(yd, dev)
+        xd = torch.from_numpy(cd.x).view(torch.bfloat16).to(dev)
+        hd = torch.from_numpy(cd.history).view(torch.bfloat16).to(dev)
+        wd = torch.from_numpy(cd.w).to(dev)
+        st = dd_["s0"].clone()
+        qd, kd, vd = torch.empty_like(dd_["q"]), torch.empty_like(dd_["k"]), torch.empty_like(dd_["v"])
+        od = torch.empty_like(dd_["v"])
+
+        def conv_decode():
+            gdn.gdn_conv_prologue(xd, wd, hd, None, num_qk_heads=hqk, num_v_heads=hv, num_seqs=n, silu=True,
+                                  qk_l2norm=True, q=qd, k=kd, v=vd, conv_state_out=hd)
+            gdn.gdn_decode_step(qd, kd, vd, dd_["g"], dd_["beta"], st, out=od)
+
+        dms_, dkern_ = time_calls(conv_decode, args.steps, max(2, args.warmup // 4), torch)
+        result["conv_prologue"]["decode_with_prologue"] = {
+            "workload": cd.name, "ms_per_step": dms_, "tokens_per_s": n / (dms_ / 1e3),
+            "kernels_ms_per_launch": {k_: v_[1] for k_, v_ in dkern_.items()}}
+        log(f"[bench] decode with the prologue {dms_:.3f} ms/step")
+        del dd_, xd, hd, wd, st, qd, kd, vd, od
+        torch.cuda.empty_cache()
 
     # Launch overhead of a short prefill (the 4,096-token layer: three launches of ~0.04 ms and the
     # combine), eager calls against replays of a captured graph.

@@ -299,6 +299,45 @@ gdn_status_t gdn_backward(const void* q, const void* k, const void* v,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Input prologue: the short causal convolution in front of the mixer. The
+ * model card (page "Qwen3-Next-80B-A3B-Instruct", section "Quickstart")
+ * points to the causal-conv1d kernels beside flash-linear-attention without
+ * saying what they convolve; the library's reading is a depthwise causal 1-D
+ * convolution over the mixer's input channels, with each channel's own K taps:
+ *
+ *     y_t[c] = sum_{i=0}^{K-1} weight[c][i] * x_{t-K+1+i}[c]
+ *
+ * (tap K-1 multiplies the current token), optionally followed by SiLU
+ * y * sigmoid(y), then split into the q, k and v arrays the mixer reads and,
+ * with GDN_FLAG_QK_L2NORM, the L2 normalisation of each q and k head, so the
+ * outputs feed gdn_prefill / gdn_decode_step directly.
+ *   x               [total_tokens, C] dtype, C = 2 Hqk d + Hv d: channel c is
+ *                   q (c < Hqk d, head c / d), then k, then v
+ *   weight          [C, K] float, 1 <= K <= 4
+ *   conv_state_in   [num_seqs, K - 1, C] dtype: each sequence's history, the
+ *                   K - 1 inputs before its first token, oldest first; NULL
+ *                   means zeros (a sequence's start)
+ *   cu_seqlens      [num_seqs + 1] device int32 offsets, or NULL: num_seqs
+ *                   sequences of total_tokens / num_seqs tokens each (one
+ *                   token per sequence is a decode step)
+ *   q, k, v         outputs [T, Hqk, d], [T, Hqk, d], [T, Hv, d], dtype
+ *   conv_state_out  [num_seqs, K - 1, C] dtype, or NULL: each sequence's last
+ *                   K - 1 inputs (reaching into conv_state_in when it is
+ *                   shorter than K - 1). May alias conv_state_in: outputs are
+ *                   computed first, the new history written by a second launch.
+ * Flags: GDN_FLAG_CONV_SILU, GDN_FLAG_QK_L2NORM (1e-6 inside the square root).
+ * d = d_k = d_v in {16, 32, 64, 128}. Errors: GDN_ERR_INVALID_ARG for null
+ * pointers, K outside [1, 4] with K > 4 reported as GDN_ERR_UNSUPPORTED,
+ * total_tokens not a multiple of num_seqs without cu_seqlens, or unknown flags.
+ */
+#define GDN_FLAG_CONV_SILU 2u
+gdn_status_t gdn_conv_prologue(const void* x, const float* weight, const void* conv_state_in,
+                               const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                               int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k, int32_t d_v,
+                               int32_t kernel_size, gdn_dtype_t dtype, uint32_t flags,
+                               void* q, void* k, void* v, void* conv_state_out, void* stream);
+
+/*
  * Instrumentation (for benchmarks and profiling; process-global, not
  * thread-safe, not for graph capture). After gdn_profile_start(), every kernel
  * the library launches is bracketed by a pair of HIP events recorded on the

@@ -16,13 +16,14 @@ import torch
 
 __all__ = ["gdn_prefill", "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots", "gdn_decode_multi",
            "gdn_prefill_ex", "gdn_decode_ex", "GDN_FLAG_QK_L2NORM", "gdn_backward", "gdn_backward_workspace_size",
-           "gdn_prefill_workspace_size", "gdn_prefill_segment_chunks",
+           "gdn_prefill_workspace_size", "gdn_prefill_segment_chunks", "gdn_conv_prologue", "GDN_FLAG_CONV_SILU",
            "gdn_status_string",
            "gdn_build_info", "gdn_profile_start", "gdn_profile_stop", "GDN_BF16", "GDN_FP32", "GdnError", "library_path"]
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(5)
 GDN_BF16, GDN_FP32 = 0, 1
 GDN_FLAG_QK_L2NORM = 1
+GDN_FLAG_CONV_SILU = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libgdn.so")
@@ -73,6 +74,9 @@ def _load():
             lib.gdn_prefill_slots.restype = ctypes.c_int
             lib.gdn_prefill_slots.argtypes = ([_vp] * 8 + [_i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                                           ctypes.c_int, _vp, _vp, _sz, _vp])
+            lib.gdn_conv_prologue.restype = ctypes.c_int
+            lib.gdn_conv_prologue.argtypes = ([_vp] * 4 + [_i32, _i64] + [_i32] * 5 + [ctypes.c_int, ctypes.c_uint32]
+                                              + [_vp] * 5)
             lib.gdn_status_string.restype = ctypes.c_char_p
             lib.gdn_status_string.argtypes = [ctypes.c_int]
             lib.gdn_build_info.restype = ctypes.c_char_p
@@ -471,3 +475,50 @@ def gdn_backward(q, k, v, g, beta, d_out, initial_state=None, cu_seqlens=None, d
     if st != GDN_OK:
         raise GdnError(st, "gdn_backward")
     return res
+
+
+def gdn_conv_prologue(x, weight, conv_state=None, cu_seqlens=None, *, num_qk_heads: int, num_v_heads: int,
+                      num_seqs: int | None = None, silu: bool = False, qk_l2norm: bool = False, q=None, k=None,
+                      v=None, conv_state_out=None, stream=None):
+    """Short causal convolution + optional SiLU + split into q, k, v (+ optional q/k L2 norm).
+
+    x [T, C] bf16 or fp32 with C = 2 Hqk d + Hv d (q, k, v channels side by side), weight [C, K] fp32,
+    conv_state [N, K - 1, C] (dtype of x) or None (zero history), cu_seqlens int32 [N + 1] or None
+    (num_seqs equal-length sequences; default one). conv_state_out: None (not written), True (allocate)
+    or a tensor (may be conv_state itself). Returns (q, k, v, conv_state_out)."""
+    dev = x.device
+    _check(x, "x", device=dev)
+    dt = _dtype_code(x)
+    _check(weight, "weight", torch.float32, dev)
+    _check(conv_state, "conv_state", x.dtype, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if x.dim() != 2 or weight.dim() != 2:
+        raise ValueError(f"x must be [T, C] and weight [C, K], got {list(x.shape)} and {list(weight.shape)}")
+    T, C = x.shape
+    K = weight.shape[1]
+    hqk, hv = int(num_qk_heads), int(num_v_heads)
+    if C % (2 * hqk + hv):
+        raise ValueError(f"{C} channels are not 2 * {hqk} + {hv} heads of one size")
+    d = C // (2 * hqk + hv)
+    _expect(weight, "weight", (C, K))
+    n = _seq_count(cu_seqlens) if cu_seqlens is not None else (1 if num_seqs is None else int(num_seqs))
+    _expect(conv_state, "conv_state", (n, K - 1, C))
+    if conv_state_out is True:
+        conv_state_out = torch.empty((n, K - 1, C), dtype=x.dtype, device=dev)
+    elif conv_state_out is False:
+        conv_state_out = None
+    _check(conv_state_out, "conv_state_out", x.dtype, dev)
+    _expect(conv_state_out, "conv_state_out", (n, K - 1, C))
+    q = torch.empty((T, hqk, d), dtype=x.dtype, device=dev) if q is None else q
+    k = torch.empty((T, hqk, d), dtype=x.dtype, device=dev) if k is None else k
+    v = torch.empty((T, hv, d), dtype=x.dtype, device=dev) if v is None else v
+    for name, t, shp in (("q", q, (T, hqk, d)), ("k", k, (T, hqk, d)), ("v", v, (T, hv, d))):
+        _check(t, name, x.dtype, dev)
+        _expect(t, name, shp)
+    flags = (GDN_FLAG_CONV_SILU if silu else 0) | (GDN_FLAG_QK_L2NORM if qk_l2norm else 0)
+    st = _load().gdn_conv_prologue(_ptr(x), _ptr(weight), _ptr(conv_state), _ptr(cu_seqlens), n, T, hqk, hv, d, d,
+                                   K, dt, flags, _ptr(q), _ptr(k), _ptr(v), _ptr(conv_state_out),
+                                   _stream(stream, dev))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_conv_prologue")
+    return q, k, v, conv_state_out

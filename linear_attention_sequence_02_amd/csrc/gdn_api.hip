@@ -249,6 +249,31 @@ gdn_status_t gdn_backward(const void* q, const void* k, const void* v, const flo
     return hip_status(gdn::launch_backward(a, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status_t gdn_conv_prologue(const void* x, const float* weight, const void* conv_state_in,
+                               const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                               int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k, int32_t d_v,
+                               int32_t kernel_size, gdn_dtype_t dtype, uint32_t flags,
+                               void* q, void* k, void* v, void* conv_state_out, void* stream) {
+    if (num_qk_heads <= 0 || num_v_heads <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_INVALID_ARG;
+    if (dtype != GDN_BF16 && dtype != GDN_FP32) return GDN_ERR_INVALID_ARG;
+    if (flags & ~(GDN_FLAG_QK_L2NORM | GDN_FLAG_CONV_SILU)) return GDN_ERR_INVALID_ARG;
+    if (d_k != d_v || !fp32_head_size_ok(d_k)) return GDN_ERR_UNSUPPORTED;
+    if (kernel_size < 1) return GDN_ERR_INVALID_ARG;
+    if (kernel_size > 4) return GDN_ERR_UNSUPPORTED;
+    if (total_tokens < 0 || num_seqs < 0) return GDN_ERR_INVALID_ARG;
+    if (total_tokens > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return total_tokens == 0 ? GDN_OK : GDN_ERR_INVALID_ARG;
+    if (cu_seqlens == nullptr && total_tokens % num_seqs != 0) return GDN_ERR_INVALID_ARG;
+    if (total_tokens > 0 && (!x || !weight || !q || !k || !v)) return GDN_ERR_INVALID_ARG;
+    gdn::ConvPrologueArgs a;
+    a.x = x; a.weight = weight; a.conv_state_in = conv_state_in; a.conv_state_out = conv_state_out;
+    a.cu_seqlens = cu_seqlens; a.q = q; a.k = k; a.v = v; a.total_tokens = total_tokens; a.num_seqs = num_seqs;
+    a.num_qk_heads = num_qk_heads; a.num_v_heads = num_v_heads; a.d = d_k; a.kernel_size = kernel_size;
+    a.silu = (flags & GDN_FLAG_CONV_SILU) != 0; a.qk_norm = (flags & GDN_FLAG_QK_L2NORM) != 0;
+    a.bf16 = (dtype == GDN_BF16);
+    return hip_status(gdn::launch_conv_prologue(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* gdn_status_string(gdn_status_t s) {
     switch (s) {
         case GDN_OK: return "GDN_OK";

@@ -83,6 +83,20 @@ struct BackwardArgs {
     bool bf16;
 };
 
+struct ConvPrologueArgs {
+    const void* x;                // [T, C] inputs, C = 2 Hqk d + Hv d (q, k, v channels)
+    const float* weight;          // [C, K]
+    const void* conv_state_in;    // [N, K - 1, C] history or null (zeros)
+    void* conv_state_out;         // [N, K - 1, C] or null; may alias conv_state_in
+    const int32_t* cu_seqlens;    // null: num_seqs sequences of total_tokens / num_seqs tokens
+    void* q;
+    void* k;
+    void* v;
+    int64_t total_tokens;
+    int32_t num_seqs, num_qk_heads, num_v_heads, d, kernel_size;
+    bool silu, qk_norm, bf16;
+};
+
 namespace prof {
 // Event pair around one kernel launch when instrumentation is on (no-op otherwise).
 void begin(hipStream_t s, const char* name);
@@ -90,6 +104,7 @@ void end(hipStream_t s);
 }  // namespace prof
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_conv_prologue(const ConvPrologueArgs& a, hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 size_t backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_v_heads, int32_t d);
 hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t stream);

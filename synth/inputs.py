@@ -302,3 +302,36 @@ def state_pool(num_slots: int, hv: int, d: int, seed: int, std: float = 0.3) -> 
     states a serving cache holds, addressed by slot)."""
     rng = np.random.default_rng(seed)
     return (std * rng.standard_normal((num_slots, hv, d, d))).astype(np.float32)
+
+
+@dataclasses.dataclass
+class ConvInputs:
+    x: np.ndarray              # [T, C] the mixer's input channels (q, k, v side by side), bf16 bits or fp32
+    w: np.ndarray              # [C, K] fp32 taps
+    history: np.ndarray | None  # [N, K - 1, C] (dtype of x) or None
+    cu_seqlens: np.ndarray
+    hqk: int
+    hv: int
+    d: int
+    dtype: str
+    name: str
+
+
+def conv_inputs(*, lengths, hqk: int, hv: int, d: int, K: int = 4, dtype: str = "bf16", seed: int = 0,
+                history: bool = True, name: str = "conv") -> ConvInputs:
+    """Inputs of the short causal convolution in front of the mixer: x ~ N(0, 1) over C = 2 Hqk d + Hv d
+    channels, taps w ~ N(0, 1) / sqrt(K), histories N(0, 1) (main generator default_rng(seed), in that
+    order)."""
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in lengths]
+    T = int(sum(lengths))
+    C = (2 * hqk + hv) * d
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    x = rng.standard_normal((T, C), dtype=np.float32)
+    w = (rng.standard_normal((C, K)) / math.sqrt(K)).astype(np.float32)
+    h = rng.standard_normal((len(lengths), K - 1, C), dtype=np.float32) if history else None
+    if dtype == "bf16":
+        x = f32_to_bf16_bits(x)
+        h = None if h is None else f32_to_bf16_bits(h)
+    return ConvInputs(x=x, w=w, history=h, cu_seqlens=cu, hqk=hqk, hv=hv, d=d, dtype=dtype, name=name)

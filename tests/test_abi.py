@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
                                          "gdn_decode_multi", "gdn_prefill_ex", "gdn_decode_ex",
                                          "gdn_backward", "gdn_backward_workspace_size",
                                          "gdn_status_string", "gdn_build_info", "gdn_profile_start",
-                                         "gdn_profile_stop"}
+                                         "gdn_profile_stop", "gdn_conv_prologue"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -260,3 +260,32 @@ def test_python_binding_raises_on_bad_dtype():
     q = torch.zeros(4, 2, 128, dtype=torch.float16)
     with pytest.raises(TypeError):
         gdn.gdn_prefill(q, q, q, q, q)
+
+
+def _conv(lib, **over):
+    a = dict(x=FAKE, w=FAKE, hin=None, cu=FAKE, n=2, T=100, hqk=16, hv=32, dk=128, dv=128, K=4, dt=gdn.GDN_BF16,
+             flags=0, q=FAKE, k=FAKE, v=FAKE, hout=None, stream=None)
+    a.update(over)
+    return lib.gdn_conv_prologue(a["x"], a["w"], a["hin"], a["cu"], a["n"], a["T"], a["hqk"], a["hv"], a["dk"],
+                                 a["dv"], a["K"], a["dt"], a["flags"], a["q"], a["k"], a["v"], a["hout"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(x=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(w=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(q=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(K=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(K=5), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dk=100, dv=100), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=64), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(flags=0x4), gdn.GDN_ERR_INVALID_ARG),
+    (dict(cu=None, n=3, T=100), gdn.GDN_ERR_INVALID_ARG),   # 100 tokens are not 3 equal sequences
+    (dict(T=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(n=0, T=5), gdn.GDN_ERR_INVALID_ARG),
+])
+def test_conv_prologue_rejects(lib, over, status):
+    assert _conv(lib, **over) == status
+
+
+def test_conv_prologue_with_no_sequences_is_a_no_op(lib):
+    assert _conv(lib, n=0, T=0) == gdn.GDN_OK

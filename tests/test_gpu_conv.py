@@ -1,0 +1,137 @@
+"""GPU input prologue (gdn_conv_prologue: short causal convolution, optional SiLU, q/k/v split,
+optional q/k L2 normalisation) against the fp64 oracle (oracle/conv.py), alone and feeding the
+prefill and decode paths. Bars: rel-L2 <= 1e-2 for bf16 outputs and 1e-4 in fp32 mode, as for the
+mixer; the new history is a copy of inputs and is compared bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_sequence_02_amd as gdn
+import oracle
+from synth import inputs as I
+from tests.gpu_util import log, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "fp32": 1e-4}
+
+
+def _dev(a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def _f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _run(c, silu, norm, use_history=True, equal_lengths=False):
+    x = _dev(c.x, c.dtype)
+    w = torch.from_numpy(c.w).cuda()
+    h = _dev(c.history, c.dtype) if (use_history and c.history is not None) else None
+    cu = None if equal_lengths else torch.from_numpy(c.cu_seqlens).cuda()
+    n = len(c.cu_seqlens) - 1
+    log(f"[gpu] gdn_conv_prologue {c.name} T={c.x.shape[0]} C={c.x.shape[1]} K={c.w.shape[1]} {c.dtype} "
+        f"silu={silu} norm={norm}")
+    q, k, v, hout = gdn.gdn_conv_prologue(x, w, h, cu, num_qk_heads=c.hqk, num_v_heads=c.hv, num_seqs=n, silu=silu,
+                                          qk_l2norm=norm, conv_state_out=True)
+    torch.cuda.synchronize()
+    return q, k, v, hout
+
+
+@pytest.mark.parametrize("dtype,d,K,silu,norm", [("bf16", 128, 4, True, True), ("bf16", 128, 4, False, False),
+                                                 ("fp32", 16, 3, True, False), ("fp32", 64, 2, False, True),
+                                                 ("fp32", 32, 1, True, True), ("bf16", 16, 4, False, True)])
+def test_conv_prologue(dtype, d, K, silu, norm):
+    lengths = [1, 2, 3, 0, 31, 32, 33, 100, 64, 7]
+    c = I.conv_inputs(lengths=lengths, hqk=2, hv=4, d=d, K=K, dtype=dtype, seed=300 + d + K, name=f"conv_{dtype}_d{d}_K{K}")
+    q, k, v, hout = _run(c, silu, norm)
+    rq, rk, rv, rh = oracle.conv_prologue(c.x, c.w, c.hqk, c.hv, d, d, c.cu_seqlens, c.history, silu_act=silu,
+                                          qk_l2norm=norm)
+    eq, ek, ev = rel_l2(_f64(q), rq), rel_l2(_f64(k), rk), rel_l2(_f64(v), rv)
+    log(f"[parity] {c.name}: q {eq:.3e} k {ek:.3e} v {ev:.3e}")
+    assert max(eq, ek, ev) <= TOL[dtype]
+    # the new history is a copy of inputs (or of the old history): exact
+    got_h = hout.view(torch.int16).cpu().numpy() if dtype == "bf16" else hout.cpu().numpy()
+    ref_h = (oracle.upcast(I.f32_to_bf16_bits(rh.astype(np.float32))) if dtype == "bf16" else rh)
+    if dtype == "bf16":
+        assert np.array_equal(got_h.view(np.uint16), I.f32_to_bf16_bits(rh.astype(np.float32)))
+    else:
+        assert np.array_equal(got_h.astype(np.float64), ref_h)
+
+
+def test_conv_prologue_layer_shape_without_history():
+    # The layer's channel count (2 x 16 x 128 + 32 x 128 = 8192) over 4,096 tokens, zero history.
+    c = I.conv_inputs(lengths=[4096], hqk=16, hv=32, d=128, K=4, dtype="bf16", seed=310, history=False,
+                      name="conv_layer_T4096")
+    q, k, v, hout = _run(c, True, True)
+    rq, rk, rv, rh = oracle.conv_prologue(c.x, c.w, 16, 32, 128, 128, c.cu_seqlens, None, silu_act=True,
+                                          qk_l2norm=True)
+    eq, ek, ev = rel_l2(_f64(q), rq), rel_l2(_f64(k), rk), rel_l2(_f64(v), rv)
+    log(f"[parity] {c.name}: q {eq:.3e} k {ek:.3e} v {ev:.3e}")
+    assert max(eq, ek, ev) <= 1e-2
+    assert np.array_equal(hout.view(torch.int16).cpu().numpy().view(np.uint16), c.x[-3:][None])
+
+
+def test_conv_history_in_place():
+    # conv_state_out aliasing conv_state: outputs still see the old history, the array ends up new.
+    c = I.conv_inputs(lengths=[5, 1, 0, 40], hqk=2, hv=4, d=128, K=4, dtype="bf16", seed=320, name="conv_inplace")
+    x = _dev(c.x, "bf16")
+    w = torch.from_numpy(c.w).cuda()
+    h = _dev(c.history, "bf16")
+    cu = torch.from_numpy(c.cu_seqlens).cuda()
+    log("[gpu] gdn_conv_prologue in place")
+    q, k, v, hout = gdn.gdn_conv_prologue(x, w, h, cu, num_qk_heads=2, num_v_heads=4, silu=True, conv_state_out=h)
+    torch.cuda.synchronize()
+    assert hout.data_ptr() == h.data_ptr()
+    rq, rk, rv, rh = oracle.conv_prologue(c.x, c.w, 2, 4, 128, 128, c.cu_seqlens, c.history, silu_act=True)
+    assert max(rel_l2(_f64(q), rq), rel_l2(_f64(k), rk), rel_l2(_f64(v), rv)) <= 1e-2
+    assert np.array_equal(h.view(torch.int16).cpu().numpy().view(np.uint16),
+                          I.f32_to_bf16_bits(rh.astype(np.float32)))
+
+
+def test_conv_then_prefill_then_decode():
+    """The prologue feeding the mixer: a varlen prefill of 3 sequences from zero history and zero
+    state, then 3 decode steps per sequence (one token per sequence per step) continuing both the
+    convolution history and the mixer state, against the oracle run on the whole sequences."""
+    hqk, hv, d, K = 2, 4, 128, 4
+    lengths = [70, 129, 5]
+    steps = 3
+    N = len(lengths)
+    total = [L + steps for L in lengths]
+    c = I.conv_inputs(lengths=total, hqk=hqk, hv=hv, d=d, K=K, dtype="bf16", seed=330, history=False,
+                      name="conv_prefill_decode")
+    gb = I.draw(lengths=total, hqk=hqk, hv=hv, dk=d, dtype="bf16", seed=331)   # g, beta only
+    cu_all = c.cu_seqlens
+    pre_rows = np.concatenate([np.arange(cu_all[n], cu_all[n] + lengths[n]) for n in range(N)])
+    cu_pre = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    w = torch.from_numpy(c.w).cuda()
+    # prefill: prologue then mixer
+    log("[gpu] conv prologue + prefill")
+    q, k, v, hist = gdn.gdn_conv_prologue(_dev(c.x[pre_rows], "bf16"), w, None, torch.from_numpy(cu_pre).cuda(),
+                                          num_qk_heads=hqk, num_v_heads=hv, silu=True, qk_l2norm=True,
+                                          conv_state_out=True)
+    out_pre, state = gdn.gdn_prefill(q, k, v, torch.from_numpy(gb.g[pre_rows]).cuda(),
+                                     torch.from_numpy(gb.beta[pre_rows]).cuda(), None,
+                                     torch.from_numpy(cu_pre).cuda())
+    outs = []
+    for s in range(steps):
+        rows = np.array([cu_all[n] + lengths[n] + s for n in range(N)])
+        log(f"[gpu] conv prologue + decode step {s}")
+        qd, kd, vd, hist = gdn.gdn_conv_prologue(_dev(c.x[rows], "bf16"), w, hist, None, num_qk_heads=hqk,
+                                                 num_v_heads=hv, num_seqs=N, silu=True, qk_l2norm=True,
+                                                 conv_state_out=hist)
+        outs.append(gdn.gdn_decode_step(qd, kd, vd, torch.from_numpy(gb.g[rows]).cuda(),
+                                        torch.from_numpy(gb.beta[rows]).cuda(), state))
+    torch.cuda.synchronize()
+    # oracle on the whole sequences
+    rq, rk, rv, _ = oracle.conv_prologue(c.x, c.w, hqk, hv, d, d, cu_all, None, silu_act=True, qk_l2norm=True)
+    ro, rf = oracle.recurrent(rq, rk, rv, gb.g.astype(np.float64), gb.beta.astype(np.float64), None, cu_all)
+    got = np.zeros_like(ro)
+    got[pre_rows] = _f64(out_pre)
+    for s in range(steps):
+        got[[cu_all[n] + lengths[n] + s for n in range(N)]] = _f64(outs[s])
+    eo, ef = rel_l2(got, ro), rel_l2(state.cpu().numpy(), rf)
+    log(f"[parity] conv+prefill+decode: out {eo:.3e} state {ef:.3e}")
+    assert eo <= 1e-2 and ef <= 1e-2
