@@ -50,7 +50,8 @@ typedef enum {
     GDN_ERR_INVALID_ARG = 1,   /* null required pointer, bad count or size */
     GDN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (dtype / head size) */
     GDN_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
-    GDN_ERR_HIP = 4            /* a HIP launch failed (the status string has no detail) */
+    GDN_ERR_HIP = 4,           /* a HIP launch failed (the status string has no detail) */
+    GDN_ERR_SCRATCH_LIMIT = 5  /* gdn_prefill_noalloc: the call needs more workspace than its static array */
 } gdn_status_t;
 
 typedef enum {
@@ -297,6 +298,28 @@ gdn_status_t gdn_backward(const void* q, const void* k, const void* v,
                           float* dq, float* dk, float* dv, float* dg, float* dbeta,
                           float* d_initial_state,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_prefill for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and errors are gdn_prefill's, without the workspace: the
+ * bf16 path's segment workspace is a static device array of
+ * GDN_PREFILL_NOALLOC_SCRATCH_BYTES held by every GPU the library is loaded on
+ * until the process ends. A call whose gdn_prefill_workspace_size exceeds it
+ * returns GDN_ERR_SCRATCH_LIMIT before anything is enqueued (with 32 V heads it
+ * covers one sequence of any length, and up to about 10 long sequences per
+ * call). The entry point allocates nothing. All calls on one GPU share its
+ * array: calls that may overlap on one GPU (other streams, other threads
+ * without ordering) race and must be serialised by the caller.
+ */
+#define GDN_PREFILL_NOALLOC_SCRATCH_BYTES (192ull << 20)
+gdn_status_t gdn_prefill_noalloc(const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta,
+                                 const float* initial_state,
+                                 const int32_t* cu_seqlens, int32_t num_seqs,
+                                 int64_t total_tokens, int32_t num_qk_heads, int32_t num_v_heads,
+                                 int32_t d_k, int32_t d_v, float scale, gdn_dtype_t dtype,
+                                 void* out, float* final_state, void* stream);
 
 /*
  * Input prologue: the short causal convolution in front of the mixer. The

@@ -14,13 +14,14 @@ import threading
 
 import torch
 
-__all__ = ["gdn_prefill", "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots", "gdn_decode_multi",
+__all__ = ["gdn_prefill", "gdn_prefill_noalloc", "GDN_ERR_SCRATCH_LIMIT", "GDN_PREFILL_NOALLOC_SCRATCH_BYTES", "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots", "gdn_decode_multi",
            "gdn_prefill_ex", "gdn_decode_ex", "GDN_FLAG_QK_L2NORM", "gdn_backward", "gdn_backward_workspace_size",
            "gdn_prefill_workspace_size", "gdn_prefill_segment_chunks", "gdn_conv_prologue", "GDN_FLAG_CONV_SILU",
            "gdn_status_string",
            "gdn_build_info", "gdn_profile_start", "gdn_profile_stop", "GDN_BF16", "GDN_FP32", "GdnError", "library_path"]
 
-GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(5)
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP, GDN_ERR_SCRATCH_LIMIT = range(6)
+GDN_PREFILL_NOALLOC_SCRATCH_BYTES = 192 << 20
 GDN_BF16, GDN_FP32 = 0, 1
 GDN_FLAG_QK_L2NORM = 1
 GDN_FLAG_CONV_SILU = 2
@@ -74,6 +75,9 @@ def _load():
             lib.gdn_prefill_slots.restype = ctypes.c_int
             lib.gdn_prefill_slots.argtypes = ([_vp] * 8 + [_i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                                           ctypes.c_int, _vp, _vp, _sz, _vp])
+            lib.gdn_prefill_noalloc.restype = ctypes.c_int
+            lib.gdn_prefill_noalloc.argtypes = ([_vp] * 7 + [_i32, _i64, _i32, _i32, _i32, _i32, _f32, ctypes.c_int]
+                                                + [_vp, _vp, _vp])
             lib.gdn_conv_prologue.restype = ctypes.c_int
             lib.gdn_conv_prologue.argtypes = ([_vp] * 4 + [_i32, _i64] + [_i32] * 5 + [ctypes.c_int, ctypes.c_uint32]
                                               + [_vp] * 5)
@@ -522,3 +526,31 @@ def gdn_conv_prologue(x, weight, conv_state=None, cu_seqlens=None, *, num_qk_hea
     if st != GDN_OK:
         raise GdnError(st, "gdn_conv_prologue")
     return q, k, v, conv_state_out
+
+
+def gdn_prefill_noalloc(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, out, final_state=None,
+                        scale: float = 1.0, stream=None):
+    """gdn_prefill without a workspace argument (the library's static device array serves as the
+    workspace, so the call allocates nothing). `out` must be given; final_state may be None (not
+    written). Calls that may overlap on one GPU must be serialised by the caller. Returns
+    (out, final_state)."""
+    dev = q.device
+    _check(q, "q", device=dev)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        _check(t, name, q.dtype, dev)
+    for name, t in (("g", g), ("beta", beta), ("initial_state", initial_state), ("final_state", final_state)):
+        _check(t, name, torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if out is None:
+        raise ValueError("gdn_prefill_noalloc needs `out` (it allocates nothing)")
+    T, hqk, dk, hv, dv = _token_shapes(q, k, v, g, beta, out)
+    n = 1 if cu_seqlens is None else _seq_count(cu_seqlens)
+    _expect(initial_state, "initial_state", (n, hv, dv, dk))
+    _expect(final_state, "final_state", (n, hv, dv, dk))
+    st = _load().gdn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                     _ptr(cu_seqlens), n, T, hqk, hv, dk, dv, float(scale), dt, _ptr(out),
+                                     _ptr(final_state), _stream(stream, dev))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_prefill_noalloc")
+    return out, final_state

@@ -281,6 +281,8 @@ const char* gdn_status_string(gdn_status_t s) {
         case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: dtype or head size not supported";
         case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
         case GDN_ERR_HIP: return "GDN_ERR_HIP: HIP kernel launch failed";
+        case GDN_ERR_SCRATCH_LIMIT:
+            return "GDN_ERR_SCRATCH_LIMIT: the call needs more workspace than gdn_prefill_noalloc's static array";
         default: return "GDN: unknown status";
     }
 }

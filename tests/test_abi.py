@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
                                          "gdn_decode_multi", "gdn_prefill_ex", "gdn_decode_ex",
                                          "gdn_backward", "gdn_backward_workspace_size",
                                          "gdn_status_string", "gdn_build_info", "gdn_profile_start",
-                                         "gdn_profile_stop", "gdn_conv_prologue"}
+                                         "gdn_profile_stop", "gdn_conv_prologue", "gdn_prefill_noalloc"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -289,3 +289,17 @@ def test_conv_prologue_rejects(lib, over, status):
 
 def test_conv_prologue_with_no_sequences_is_a_no_op(lib):
     assert _conv(lib, n=0, T=0) == gdn.GDN_OK
+
+
+def test_noalloc_rejects_sizes_beyond_its_array(lib):
+    # 2,000 sequences of the layer's head shape need far more segment workspace than the static array.
+    need = gdn.gdn_prefill_workspace_size(2_000_000, 2000, 16, 32, 128, 128, gdn.GDN_BF16)
+    assert need > gdn.GDN_PREFILL_NOALLOC_SCRATCH_BYTES
+    st = lib.gdn_prefill_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 2000, 2_000_000, 16, 32, 128, 128, 1.0,
+                                 gdn.GDN_BF16, FAKE, None, None)
+    assert st == gdn.GDN_ERR_SCRATCH_LIMIT
+    assert "static array" in gdn.gdn_status_string(st)
+    # invalid arguments are still gdn_prefill's errors
+    st = lib.gdn_prefill_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 2, 100, 3, 32, 128, 128, 1.0,
+                                 gdn.GDN_BF16, FAKE, None, None)
+    assert st == gdn.GDN_ERR_INVALID_ARG
