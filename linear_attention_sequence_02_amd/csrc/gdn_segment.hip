@@ -127,7 +127,8 @@ __device__ __forceinline__ void buf_st_b32(uint32_t x, rsrc_t r, uint32_t off) {
 // beta (row = lane) of the chunk one ahead.
 struct ProdRegs {
     u32x4 k[4], q[4];
-    float g, b;
+    float g, b;     // the chunk whose factors are built next
+    float gn, bn;   // the chunk after it, requested a whole chunk step ahead
 };
 
 // Rows past the end of a chunk re-read its last row (they are zeroed when
@@ -150,8 +151,8 @@ __device__ __forceinline__ void prod_fetch_kq(ProdRegs& pr, const uint16_t* kc, 
 __device__ __forceinline__ void prod_fetch_gb(ProdRegs& pr, const float* gc, const float* bc, int nc, int hv,
                                               int lane) {
     const uint32_t off = (uint32_t)(lane * hv) * 4u;
-    pr.g = __builtin_bit_cast(float, buf_ld_b32(chunk_rsrc(uniform_ptr(gc), (int64_t)nc * hv * 4), off));
-    pr.b = __builtin_bit_cast(float, buf_ld_b32(chunk_rsrc(uniform_ptr(bc), (int64_t)nc * hv * 4), off));
+    pr.gn = __builtin_bit_cast(float, buf_ld_b32(chunk_rsrc(uniform_ptr(gc), (int64_t)nc * hv * 4), off));
+    pr.bn = __builtin_bit_cast(float, buf_ld_b32(chunk_rsrc(uniform_ptr(bc), (int64_t)nc * hv * 4), off));
 }
 
 // In-kernel L2 normalisation of one 8-element piece of a k or q row: the 16
@@ -679,27 +680,34 @@ __device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A
         if (nchunks > 0) {
             fetch_kq(c_begin);
             fetch_gb(c_begin);
+            pr.g = pr.gn;
+            pr.b = pr.bn;
             prod_stage_kq<MODE>(sm, 0, pr, pl, A.qk_norm);
             fetch_kq(clampc(c_begin + 1));
             if (nchunks > 1) prod_stage_kq<MODE>(sm, 1, pr, pl, A.qk_norm);
         }
         lds_barrier();
         if (nchunks > 0) {
+            fetch_gb(clampc(c_begin + 1));
             prod_factors<MODE>(sm, 0, sm.F[0], pr, chunk_nc(c_begin), scale, pw, lane);
             fetch_kq(clampc(c_begin + 2));
-            fetch_gb(clampc(c_begin + 1));
+            pr.g = pr.gn;
+            pr.b = pr.bn;
         }
         lds_barrier();
         for (int64_t i = 0; i < nchunks; ++i) {
             const int64_t c = c_begin + i;
+            // g and beta of chunk c + 2, a whole step before its factors; then
             // chunk c + 1: factors (its tiles were staged two steps ago);
-            // chunk c + 2: tiles from registers to LDS; then the next loads.
+            // chunk c + 2: tiles from registers to LDS; then the next K/Q loads.
+            fetch_gb(clampc(c + 2));
             if (i + 1 < nchunks)
                 prod_factors<MODE>(sm, (int)((i + 1) % 3), sm.F[(i + 1) & 1], pr, chunk_nc(c + 1), scale, pw,
                                    lane);
             if (i + 2 < nchunks) prod_stage_kq<MODE>(sm, (int)((i + 2) % 3), pr, pl, A.qk_norm);
             fetch_kq(clampc(c + 3));
-            fetch_gb(clampc(c + 2));
+            pr.g = pr.gn;
+            pr.b = pr.bn;
             lds_barrier();
         }
         return;
