@@ -35,6 +35,8 @@ namespace gdn {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int kTokBatch = 16;   // multi-token decode: tokens staged in LDS at a time
+
 template <int D, bool BF16, bool QKN>
 __global__ __launch_bounds__(512) void decode_step_kernel(
     const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
@@ -205,34 +207,17 @@ __global__ __launch_bounds__(512) void decode_multi_kernel(
         }
         return;
     }
-    // One token's inputs for this lane: k and q slices, the value of each owned
-    // row, g and beta. Token t + 1's are requested before token t is computed.
-    using raw_t = typename std::conditional<BF16, uint2, float4>::type;
-    struct TokIn {
-        raw_t kraw[4], qraw[4];
-        float vi[R];
-        float g, b;
-    };
-    auto load_tok = [&](int t, TokIn& in) {
-        const int64_t tok = (int64_t)n * num_tokens + t;
-        const int64_t qk_base = (tok * num_qk_heads + hq) * D;
-        const raw_t* k2 = reinterpret_cast<const raw_t*>(reinterpret_cast<const char*>(k_) + qk_base * (BF16 ? 2 : 4));
-        const raw_t* q2 = reinterpret_cast<const raw_t*>(reinterpret_cast<const char*>(q_) + qk_base * (BF16 ? 2 : 4));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            in.kraw[i] = k2[c + L * i];
-            in.qraw[i] = q2[c + L * i];
-        }
-        const int64_t gb = tok * num_v_heads + h;
-#pragma unroll
-        for (int m = 0; m < R; ++m) {
-            const int row = r0 + m * ROWS_PER_PASS;
-            if constexpr (BF16) in.vi[m] = bf16_bits_to_float(reinterpret_cast<const uint16_t*>(v_)[gb * D + row]);
-            else in.vi[m] = reinterpret_cast<const float*>(v_)[gb * D + row];
-        }
-        in.g = g[gb];
-        in.b = beta[gb];
-    };
+    // The tokens' inputs (k and q of the QK head, v of the V head, g, beta) are
+    // staged in LDS by the whole workgroup, kTokBatch tokens at a time, right
+    // after the state loads are issued. Rows of the state are independent, so
+    // each thread runs all staged tokens on its first row, stores it, then on
+    // its second row: the first row's work and store overlap the second row's
+    // load, which would otherwise all wait for the slowest of them.
+    using word_t = typename std::conditional<BF16, uint2, float4>::type;   // 4 elements of k or q
+    constexpr int KQW = D / 4;                                              // words per k (or q) row
+    __shared__ word_t s_k[kTokBatch][KQW], s_q[kTokBatch][KQW];
+    __shared__ float s_v[kTokBatch][D];
+    __shared__ float s_g[kTokBatch], s_b[kTokBatch];
 
     f32x4* S = reinterpret_cast<f32x4*>(state + (srow * num_v_heads + h) * (int64_t)D * D);
     f32x4 s[R][4];
@@ -241,90 +226,109 @@ __global__ __launch_bounds__(512) void decode_multi_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             s[m][i] = __builtin_nontemporal_load(&S[(r0 + m * ROWS_PER_PASS) * (D / 4) + c + L * i]);
-    TokIn cur, nxt;
-    load_tok(0, cur);
 
-    for (int t = 0; t < num_tokens; ++t) {
-        if (t + 1 < num_tokens) load_tok(t + 1, nxt);
-        const int64_t gb = ((int64_t)n * num_tokens + t) * num_v_heads + h;
-        // Key / query element e of this lane's slice i (bf16: from the packed bits).
-        auto kf = [&](int i, int e) {
-            if constexpr (BF16) {
-                const uint32_t w = (e < 2) ? cur.kraw[i].x : cur.kraw[i].y;
-                return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
-            } else {
-                return e == 0 ? cur.kraw[i].x : e == 1 ? cur.kraw[i].y : e == 2 ? cur.kraw[i].z : cur.kraw[i].w;
-            }
-        };
-        auto qf = [&](int i, int e) {
-            if constexpr (BF16) {
-                const uint32_t w = (e < 2) ? cur.qraw[i].x : cur.qraw[i].y;
-                return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
-            } else {
-                return e == 0 ? cur.qraw[i].x : e == 1 ? cur.qraw[i].y : e == 2 ? cur.qraw[i].z : cur.qraw[i].w;
-            }
-        };
-        const float alpha = exp_nonpos(cur.g);
-        float rk = 1.f, rq = 1.f;   // in-kernel L2 normalisation factors (1 when off)
-        if constexpr (QKN) {
-            float nk = 0.f, nq = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    nk = fmaf(kf(i, e), kf(i, e), nk);
-                    nq = fmaf(qf(i, e), qf(i, e), nq);
-                }
-            rk = rsqrtf(group_sum<L>(nk) + kQkNormEps);
-            rq = rsqrtf(group_sum<L>(nq) + kQkNormEps);
+    for (int t0 = 0; t0 < num_tokens; t0 += kTokBatch) {
+        const int nb = (num_tokens - t0 < kTokBatch) ? num_tokens - t0 : kTokBatch;
+        if (t0 > 0) __syncthreads();   // the previous batch's LDS reads are done
+        for (int w = tid; w < nb * KQW; w += NT) {
+            const int tt = w / KQW, j = w % KQW;
+            const int64_t tok = (int64_t)n * num_tokens + t0 + tt;
+            const int64_t qk_base = (tok * num_qk_heads + hq) * D;
+            s_k[tt][j] = reinterpret_cast<const word_t*>(reinterpret_cast<const char*>(k_) + qk_base * (BF16 ? 2 : 4))[j];
+            s_q[tt][j] = reinterpret_cast<const word_t*>(reinterpret_cast<const char*>(q_) + qk_base * (BF16 ? 2 : 4))[j];
         }
-        float kq = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kq = fmaf(kf(i, e), qf(i, e), kq);
-        kq = group_sum<L>(kq) * (rk * rq);
-        const int64_t vo_base = gb * D;
+        for (int w = tid; w < nb * D; w += NT) {
+            const int tt = w / D, j = w % D;
+            const int64_t gb = ((int64_t)n * num_tokens + t0 + tt) * num_v_heads + h;
+            if constexpr (BF16) s_v[tt][j] = bf16_bits_to_float(reinterpret_cast<const uint16_t*>(v_)[gb * D + j]);
+            else s_v[tt][j] = reinterpret_cast<const float*>(v_)[gb * D + j];
+        }
+        if (tid < nb) {
+            const int64_t gb = ((int64_t)n * num_tokens + t0 + tid) * num_v_heads + h;
+            s_g[tid] = g[gb];
+            s_b[tid] = beta[gb];
+        }
+        __syncthreads();
+
 #pragma unroll
         for (int m = 0; m < R; ++m) {
             const int row = r0 + m * ROWS_PER_PASS;
-            float a = 0.f, bq = 0.f;
+#pragma unroll 1
+            for (int tt = 0; tt < nb; ++tt) {
+                const int64_t gb = ((int64_t)n * num_tokens + t0 + tt) * num_v_heads + h;
+                word_t kraw[4], qraw[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a = fmaf(s[m][i][e], kf(i, e), a);
-                    bq = fmaf(s[m][i][e], qf(i, e), bq);
+                for (int i = 0; i < 4; ++i) {
+                    kraw[i] = s_k[tt][c + L * i];
+                    qraw[i] = s_q[tt][c + L * i];
                 }
-            a = group_sum<L>(a) * rk;
-            bq = group_sum<L>(bq) * rq;
-            const float u = cur.b * (cur.vi[m] - alpha * a);
-            const float uk = u * rk;
+                // Key / query element e of this lane's slice i (bf16: from the packed bits).
+                auto kf = [&](int i, int e) {
+                    if constexpr (BF16) {
+                        const uint32_t w = (e < 2) ? kraw[i].x : kraw[i].y;
+                        return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+                    } else {
+                        return e == 0 ? kraw[i].x : e == 1 ? kraw[i].y : e == 2 ? kraw[i].z : kraw[i].w;
+                    }
+                };
+                auto qf = [&](int i, int e) {
+                    if constexpr (BF16) {
+                        const uint32_t w = (e < 2) ? qraw[i].x : qraw[i].y;
+                        return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+                    } else {
+                        return e == 0 ? qraw[i].x : e == 1 ? qraw[i].y : e == 2 ? qraw[i].z : qraw[i].w;
+                    }
+                };
+                const float alpha = exp_nonpos(s_g[tt]);
+                const float bt = s_b[tt];
+                float rk = 1.f, rq = 1.f;   // in-kernel L2 normalisation factors (1 when off)
+                if constexpr (QKN) {
+                    float nk = 0.f, nq = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) s[m][i][e] = fmaf(alpha, s[m][i][e], uk * kf(i, e));
-            if (c == 0) {
-                const float o = scale * fmaf(alpha, bq, u * kq);
-                if constexpr (BF16) reinterpret_cast<uint16_t*>(out_)[vo_base + row] = float_to_bf16_bits(o);
-                else reinterpret_cast<float*>(out_)[vo_base + row] = o;
-            }
-        }
-        if (token_states) {
-            f32x4* TS = reinterpret_cast<f32x4*>(token_states + gb * (int64_t)D * D);
-#pragma unroll
-            for (int m = 0; m < R; ++m)
+                        for (int e = 0; e < 4; ++e) {
+                            nk = fmaf(kf(i, e), kf(i, e), nk);
+                            nq = fmaf(qf(i, e), qf(i, e), nq);
+                        }
+                    rk = rsqrtf(group_sum<L>(nk) + kQkNormEps);
+                    rq = rsqrtf(group_sum<L>(nq) + kQkNormEps);
+                }
+                float kq = 0.f, a = 0.f, bq = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    __builtin_nontemporal_store(s[m][i], &TS[(r0 + m * ROWS_PER_PASS) * (D / 4) + c + L * i]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        kq = fmaf(kf(i, e), qf(i, e), kq);
+                        a = fmaf(s[m][i][e], kf(i, e), a);
+                        bq = fmaf(s[m][i][e], qf(i, e), bq);
+                    }
+                kq = group_sum<L>(kq) * (rk * rq);
+                a = group_sum<L>(a) * rk;
+                bq = group_sum<L>(bq) * rq;
+                const float u = bt * (s_v[tt][row] - alpha * a);
+                const float uk = u * rk;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[m][i][e] = fmaf(alpha, s[m][i][e], uk * kf(i, e));
+                if (c == 0) {
+                    const float o = scale * fmaf(alpha, bq, u * kq);
+                    if constexpr (BF16) reinterpret_cast<uint16_t*>(out_)[gb * D + row] = float_to_bf16_bits(o);
+                    else reinterpret_cast<float*>(out_)[gb * D + row] = o;
+                }
+                if (token_states) {
+                    f32x4* TS = reinterpret_cast<f32x4*>(token_states + gb * (int64_t)D * D);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(s[m][i], &TS[row * (D / 4) + c + L * i]);
+                }
+            }
+            if (t0 + nb >= num_tokens) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(s[m][i], &S[row * (D / 4) + c + L * i]);
+            }
         }
-        cur = nxt;
     }
-#pragma unroll
-    for (int m = 0; m < R; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_nontemporal_store(s[m][i], &S[(r0 + m * ROWS_PER_PASS) * (D / 4) + c + L * i]);
 }
 
 template <int D, bool BF16, bool QKN>
