@@ -27,7 +27,8 @@ Roofline figures use algorithmic work only:
       warm-up calls, so the headline's steps start on a busy GPU.
   decode: 1,080,098,816 bytes per step for 256 sequences (state read + write
       plus q, k, v, g, beta, out); also on a state pool addressed by slot
-      ("decode.slots"), and as eager calls against graph replays, wall clock
+      ("decode.slots": 256 of 384 rows in seeded random order, and
+      "rows_ascending" with the same rows in ascending order), and as eager calls against graph replays, wall clock
       per step ("decode.graph_replay", 256 and 8 sequences; a graph holds 16 steps)
   multi-token decode ("decode_multi"): 4 tokens per sequence from one state,
       256 sequences: the state read and written once plus 4 tokens' inputs and
@@ -45,8 +46,15 @@ Roofline figures use algorithmic work only:
       q/k/v split and q/k L2 normalisation, against HBM at the bf16 input read
       once and q, k, v written once (2 x 2 B per token and channel); and the
       256-sequence decode step preceded by the prologue on one token each
-      ("decode_with_prologue", wall time of both launches)
-Peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8.0 TB/s.
+      ("decode_with_prologue", wall time of both launches), and the same step
+      with the prologue fused into the decode kernel ("decode_conv_fused", one
+      launch, against HBM at the state read and written once plus the token's
+      channels, the history read and written once, g, beta, out and the taps)
+Peaks: bf16 dense MFMA 2516.6 TFLOP/s, HBM 8.0 TB/s (vendor figures, the
+denominators of every fraction). "measured_peaks" gives this GPU's own limits
+beside them, from the microbenchmarks in libgdn_peaks.so: HBM copy and
+read-only streaming over 1 GiB, and the dense bf16 and fp32 MFMA issue rate
+with the shader clock observed under that load.
 "step_ms" gives the mean, median and min of the prefill step over a further pass
 with events around each call (so its mean can differ from "ms_per_step", the
 timed run's). The timed run behind `value` has no
@@ -137,6 +145,61 @@ def time_calls(fn, steps, warmup, torch, profile=True, per_step=None):
         torch.cuda.synchronize()
         per_step.extend(a.elapsed_time(b) for a, b in ev)
     return ms, {k: (c, t / c) for k, (c, t) in kernels.items()}
+
+
+def measured_peaks(torch, dev):
+    """This GPU's own limits from the microbenchmarks in libgdn_peaks.so, beside the vendor peaks (the
+    roofline fractions stay against the vendor figures): HBM copy and read-only streaming over 1 GiB
+    buffers (four times the 256 MB last-level cache), and the dense MFMA issue rate with 8 waves per
+    SIMD and 8 independent accumulators per wave (bf16 16x16x32, fp32 16x16x4), with the shader clock
+    those waves observed (core-clock ticks against the 100 MHz real-time counter, median over waves)."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "linear_attention_sequence_02_amd",
+                        "libgdn_peaks.so")
+    if not os.path.exists(path):
+        return {"error": "libgdn_peaks.so not built"}
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.peaks_copy.argtypes = [vp, vp, i64, vp]
+    lib.peaks_read.argtypes = [vp, i64, vp, vp]
+    lib.peaks_mfma.argtypes = [i32, i32, i32, vp, vp, vp]
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(launch, reps):
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            launch()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps / 1e3   # seconds per launch
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"peaks launch failed: HIP error {rc}")
+
+    nbytes = 1 << 30
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    t_copy = timed(lambda: check(lib.peaks_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh)), 10)
+    t_read = timed(lambda: check(lib.peaks_read(src.data_ptr(), nbytes, sink.data_ptr(), sh)), 10)
+    del src, dst
+    blocks = 2048                     # 8192 waves: 8 per SIMD on 1024 SIMDs
+    res = {"hbm_copy_GBps": 2 * nbytes / t_copy / 1e9, "hbm_read_GBps": nbytes / t_read / 1e9,
+           "stream_bytes": nbytes}
+    for name, bf16, iters, flop in (("mfma_bf16_16x16x32", 1, 2048, 16384), ("mfma_fp32_16x16x4", 0, 1024, 2048)):
+        fsink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        ticks = torch.zeros(blocks * 4 * 2, dtype=torch.int64, device=dev)
+        t = timed(lambda: check(lib.peaks_mfma(bf16, blocks, iters, fsink.data_ptr(), ticks.data_ptr(), sh)), 5)
+        tk = ticks.view(-1, 2).cpu().numpy().astype(np.float64)
+        clk = np.median(tk[:, 0] / np.maximum(tk[:, 1], 1.0)) * 100.0
+        res[name] = {"TFLOPs": blocks * 4 * 8 * iters * flop / t / 1e12, "clock_MHz": float(clk)}
+    return res
 
 
 def graph_vs_eager(fn, steps, torch, per_graph=16):
@@ -333,6 +396,7 @@ def main():
     ap.add_argument("--config", default=None,
                     help="time only this prefill configuration and print its record (for profiling): one of "
                          "qwen3next_gdn_prefill_T4096, qwen3next_gdn_varlen8, qwen3next_gdn_long_T262144")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the HBM / MFMA microbenchmarks")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one 256 MiB device-to-device copy (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -491,6 +555,17 @@ def main():
 
         sms, skern = time_calls(decode_slots, args.steps, args.warmup, torch)
         skms = skern.get("gdn_decode_step", (0, sms))[1]
+        # The same 256 rows with sequence n on the n-th lowest of them: rows in ascending order.
+        idx_sorted = torch.sort(idx).values.contiguous()
+        pool_s = torch.zeros_like(pool)
+        pool_s[idx_sorted.long()] = dd["s0"]
+
+        def decode_slots_sorted():
+            gdn.gdn_decode_step_slots(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], pool_s, idx_sorted, out=dout)
+
+        oms, okern = time_calls(decode_slots_sorted, args.steps, args.warmup, torch)
+        okms = okern.get("gdn_decode_step", (0, oms))[1]
+        del pool_s
         st_n = dd["s0"].clone()
 
         def decode_norm():
@@ -503,9 +578,13 @@ def main():
                                          "GB_per_s": nbytes / (qkms / 1e3) / 1e9,
                                          "frac_hbm_peak": nbytes / (qkms / 1e3) / 1e9 / PEAK_HBM_GBS}
         del st_n
-        result["decode"]["slots"] = {"pool_slots": slots, "ms_per_step": sms, "kernel_ms_per_launch": skms,
+        result["decode"]["slots"] = {"pool_slots": slots, "row_order": "seeded random",
+                                     "ms_per_step": sms, "kernel_ms_per_launch": skms,
                                      "GB_per_s": nbytes / (skms / 1e3) / 1e9,
-                                     "frac_hbm_peak": nbytes / (skms / 1e3) / 1e9 / PEAK_HBM_GBS}
+                                     "frac_hbm_peak": nbytes / (skms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                                     "rows_ascending": {"ms_per_step": oms, "kernel_ms_per_launch": okms,
+                                                        "GB_per_s": nbytes / (okms / 1e3) / 1e9,
+                                                        "frac_hbm_peak": nbytes / (okms / 1e3) / 1e9 / PEAK_HBM_GBS}}
         log(f"[bench] decode on a state pool {sms:.3f} ms/step")
         result["decode"]["graph_replay"] = {f"N{n}": graph_vs_eager(decode_slots, args.steps, torch)}
         del dd, state, dout, pool, idx
@@ -600,7 +679,28 @@ def main():
             "workload": cd.name, "ms_per_step": dms_, "tokens_per_s": n / (dms_ / 1e3),
             "kernels_ms_per_launch": {k_: v_[1] for k_, v_ in dkern_.items()}}
         log(f"[bench] decode with the prologue {dms_:.3f} ms/step")
-        del dd_, xd, hd, wd, st, qd, kd, vd, od
+        # The same step in one launch (gdn_decode_conv), the history alternating between two arrays.
+        hd2 = torch.empty_like(hd)
+        hist_pair = [hd, hd2]
+
+        def conv_decode_fused():
+            gdn.gdn_decode_conv(xd, wd, dd_["g"], dd_["beta"], st, hist_pair[0], num_qk_heads=hqk, num_v_heads=hv,
+                                conv_state_out=hist_pair[1], silu=True, qk_l2norm=True, out=od)
+            hist_pair.reverse()
+
+        fms_, fkern_ = time_calls(conv_decode_fused, args.steps, max(2, args.warmup // 4), torch)
+        fkms = fkern_.get("gdn_decode_conv", (0, fms_))[1]
+        C_ = (2 * hqk + hv) * dd
+        fbytes = (n * hv * dd * dd * 4 * 2 + n * C_ * 2 + 2 * n * (K - 1) * C_ * 2 + n * hv * 4 * 2 + n * hv * dd * 2
+                  + C_ * K * 4)
+        fgbs = fbytes / (fkms / 1e3) / 1e9
+        result["conv_prologue"]["decode_conv_fused"] = {
+            "workload": cd.name, "ms_per_step": fms_, "tokens_per_s": n / (fms_ / 1e3), "kernel_ms_per_launch": fkms,
+            "bytes_per_launch": fbytes,
+            "roofline": {"kernel": "gdn_decode_conv", "bound": "hbm", "achieved": fgbs, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": fgbs / PEAK_HBM_GBS}}
+        log(f"[bench] fused decode with the prologue {fms_:.3f} ms/step, {fgbs:.1f} GB/s")
+        del dd_, xd, hd, hd2, hist_pair, wd, st, qd, kd, vd, od
         torch.cuda.empty_cache()
 
     # Launch overhead of a short prefill (the 4,096-token layer: three launches of ~0.04 ms and the
@@ -646,6 +746,10 @@ def main():
                                            "frac": btf / PEAK_FP32_MFMA_TFLOPS}}
         log(f"[bench] backward {bms:.3f} ms/step")
         del db, gout, wsb
+
+    if not args.no_peaks:
+        result["measured_peaks"] = measured_peaks(torch, dev)
+        log(f"[bench] measured peaks {result['measured_peaks']}")
 
     if args.calibration_copy:
         a_ = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

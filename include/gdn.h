@@ -361,6 +361,36 @@ gdn_status_t gdn_conv_prologue(const void* x, const float* weight, const void* c
                                void* q, void* k, void* v, void* conv_state_out, void* stream);
 
 /*
+ * Decode step with the input prologue fused in: gdn_conv_prologue on one token
+ * per sequence followed by gdn_decode_step, in one launch (the reading of the
+ * prologue is gdn_conv_prologue's, page "Qwen3-Next-80B-A3B-Instruct", section
+ * "Quickstart"). The workgroup of (sequence n, V head h) convolves only the
+ * channels it reads (its QK head's q and k, its V head's v), applies SiLU with
+ * GDN_FLAG_CONV_SILU and the q/k L2 normalisation with GDN_FLAG_QK_L2NORM, and
+ * runs the decode step on them; q, k and v never go through HBM and stay fp32
+ * (the unfused pair rounds them to dtype in between).
+ *   x               [num_seqs, C] dtype, C = 2 Hqk d + Hv d, channel order as
+ *                   for gdn_conv_prologue (one token per sequence)
+ *   weight          [C, K] float, 1 <= K <= 4
+ *   conv_state_in   [num_seqs, K - 1, C] dtype, or NULL (zeros)
+ *   conv_state_out  [num_seqs, K - 1, C] dtype, or NULL: the new history (the
+ *                   last K - 1 inputs, the input's bits). It must not overlap
+ *                   conv_state_in, since the workgroups of the V heads that
+ *                   share a QK head read the same q/k history rows; callers
+ *                   alternate two arrays between steps.
+ *   g, beta, state, out, scale   as for gdn_decode_step (state updated in place)
+ * d = d_k = d_v in {16, 32, 64, 128}. Errors:
+ * GDN_ERR_INVALID_ARG for null pointers, Hv not a multiple of Hqk, K < 1,
+ * unknown flags or overlapping histories; GDN_ERR_UNSUPPORTED for K > 4 or
+ * another head size. num_seqs = 0 enqueues nothing.
+ */
+gdn_status_t gdn_decode_conv(const void* x, const float* weight, const void* conv_state_in,
+                             void* conv_state_out, const float* g, const float* beta, float* state,
+                             int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads,
+                             int32_t d_k, int32_t d_v, int32_t kernel_size, float scale,
+                             gdn_dtype_t dtype, uint32_t flags, void* out, void* stream);
+
+/*
  * Instrumentation (for benchmarks and profiling; process-global, not
  * thread-safe, not for graph capture). After gdn_profile_start(), every kernel
  * the library launches is bracketed by a pair of HIP events recorded on the

@@ -16,7 +16,7 @@ import torch
 
 __all__ = ["gdn_prefill", "gdn_prefill_noalloc", "GDN_ERR_SCRATCH_LIMIT", "GDN_PREFILL_NOALLOC_SCRATCH_BYTES", "gdn_decode_step", "gdn_prefill_slots", "gdn_decode_step_slots", "gdn_decode_multi",
            "gdn_prefill_ex", "gdn_decode_ex", "GDN_FLAG_QK_L2NORM", "gdn_backward", "gdn_backward_workspace_size",
-           "gdn_prefill_workspace_size", "gdn_prefill_segment_chunks", "gdn_conv_prologue", "GDN_FLAG_CONV_SILU",
+           "gdn_prefill_workspace_size", "gdn_prefill_segment_chunks", "gdn_conv_prologue", "gdn_decode_conv", "GDN_FLAG_CONV_SILU",
            "gdn_status_string",
            "gdn_build_info", "gdn_profile_start", "gdn_profile_stop", "GDN_BF16", "GDN_FP32", "GdnError", "library_path"]
 
@@ -81,6 +81,9 @@ def _load():
             lib.gdn_conv_prologue.restype = ctypes.c_int
             lib.gdn_conv_prologue.argtypes = ([_vp] * 4 + [_i32, _i64] + [_i32] * 5 + [ctypes.c_int, ctypes.c_uint32]
                                               + [_vp] * 5)
+            lib.gdn_decode_conv.restype = ctypes.c_int
+            lib.gdn_decode_conv.argtypes = ([_vp] * 7 + [_i32] * 6 + [_f32, ctypes.c_int, ctypes.c_uint32]
+                                            + [_vp, _vp])
             lib.gdn_status_string.restype = ctypes.c_char_p
             lib.gdn_status_string.argtypes = [ctypes.c_int]
             lib.gdn_build_info.restype = ctypes.c_char_p
@@ -526,6 +529,55 @@ def gdn_conv_prologue(x, weight, conv_state=None, cu_seqlens=None, *, num_qk_hea
     if st != GDN_OK:
         raise GdnError(st, "gdn_conv_prologue")
     return q, k, v, conv_state_out
+
+
+def gdn_decode_conv(x, weight, g, beta, state, conv_state=None, *, num_qk_heads: int, num_v_heads: int,
+                    conv_state_out=None, silu: bool = False, qk_l2norm: bool = False, scale: float = 1.0,
+                    out=None, stream=None):
+    """One decode step with the input prologue fused in (one launch): the causal convolution of the
+    token's q, k, v channels over each sequence's history, optional SiLU and q/k L2 normalisation,
+    then the decode step on `state` (updated in place).
+
+    x [N, C] bf16 or fp32 (C = 2 Hqk d + Hv d), weight [C, K] fp32, g and beta [N, Hv] fp32, state
+    [N, Hv, d, d] fp32, conv_state [N, K - 1, C] (dtype of x) or None (zero history). conv_state_out:
+    None (not written), True (allocate) or a tensor that must not overlap conv_state (alternate two).
+    Returns (out [N, Hv, d], conv_state_out)."""
+    dev = x.device
+    _check(x, "x", device=dev)
+    dt = _dtype_code(x)
+    _check(weight, "weight", torch.float32, dev)
+    for name, t in (("g", g), ("beta", beta), ("state", state)):
+        _check(t, name, torch.float32, dev)
+    _check(conv_state, "conv_state", x.dtype, dev)
+    if x.dim() != 2 or weight.dim() != 2:
+        raise ValueError(f"x must be [N, C] and weight [C, K], got {list(x.shape)} and {list(weight.shape)}")
+    n, C = x.shape
+    K = weight.shape[1]
+    hqk, hv = int(num_qk_heads), int(num_v_heads)
+    if C % (2 * hqk + hv):
+        raise ValueError(f"{C} channels are not 2 * {hqk} + {hv} heads of one size")
+    d = C // (2 * hqk + hv)
+    _expect(weight, "weight", (C, K))
+    _expect(g, "g", (n, hv))
+    _expect(beta, "beta", (n, hv))
+    _expect(state, "state", (n, hv, d, d))
+    _expect(conv_state, "conv_state", (n, K - 1, C))
+    if conv_state_out is True:
+        conv_state_out = torch.empty((n, K - 1, C), dtype=x.dtype, device=dev)
+    elif conv_state_out is False:
+        conv_state_out = None
+    _check(conv_state_out, "conv_state_out", x.dtype, dev)
+    _expect(conv_state_out, "conv_state_out", (n, K - 1, C))
+    out = torch.empty((n, hv, d), dtype=x.dtype, device=dev) if out is None else out
+    _check(out, "out", x.dtype, dev)
+    _expect(out, "out", (n, hv, d))
+    flags = (GDN_FLAG_CONV_SILU if silu else 0) | (GDN_FLAG_QK_L2NORM if qk_l2norm else 0)
+    st = _load().gdn_decode_conv(_ptr(x), _ptr(weight), _ptr(conv_state), _ptr(conv_state_out), _ptr(g),
+                                 _ptr(beta), _ptr(state), n, hqk, hv, d, d, K, float(scale), dt, flags, _ptr(out),
+                                 _stream(stream, dev))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_decode_conv")
+    return out, conv_state_out
 
 
 def gdn_prefill_noalloc(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, out, final_state=None,

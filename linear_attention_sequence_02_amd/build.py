@@ -8,6 +8,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
+# Microbenchmarks of the machine's limits (HBM streaming, MFMA issue rate): a
+# library of their own, loaded only by the benchmark.
+PEAKS_LIB = os.path.join(HERE, "libgdn_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 SOURCES = ["gdn_api.hip", "gdn_decode.hip", "gdn_prefill_f32.hip", "gdn_segment.hip", "gdn_profile.hip",
            "gdn_backward.hip", "gdn_conv.hip", "gdn_noalloc.hip"]
 ARCH = "gfx950"
@@ -27,9 +31,16 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every kernel source into one shared library; returns its path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+    """Compile every kernel source into libgdn.so (and the microbenchmarks into
+    libgdn_peaks.so); returns the path of libgdn.so."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(PEAKS_SOURCES, PEAKS_LIB, verbose)
+    return LIB
+
+
+def _compile(sources, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in sources] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -39,8 +50,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -274,6 +274,42 @@ gdn_status_t gdn_conv_prologue(const void* x, const float* weight, const void* c
     return hip_status(gdn::launch_conv_prologue(a, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status_t gdn_decode_conv(const void* x, const float* weight, const void* conv_state_in, void* conv_state_out,
+                             const float* g, const float* beta, float* state, int32_t num_seqs,
+                             int32_t num_qk_heads, int32_t num_v_heads, int32_t d_k, int32_t d_v,
+                             int32_t kernel_size, float scale, gdn_dtype_t dtype, uint32_t flags, void* out,
+                             void* stream) {
+    if (num_qk_heads <= 0 || num_v_heads <= 0 || d_k <= 0 || d_v <= 0 || num_seqs < 0)
+        return GDN_ERR_INVALID_ARG;
+    if (num_v_heads % num_qk_heads != 0) return GDN_ERR_INVALID_ARG;
+    if (dtype != GDN_BF16 && dtype != GDN_FP32) return GDN_ERR_INVALID_ARG;
+    if (flags & ~(GDN_FLAG_QK_L2NORM | GDN_FLAG_CONV_SILU)) return GDN_ERR_INVALID_ARG;
+    if (d_k != d_v || !fp32_head_size_ok(d_k)) return GDN_ERR_UNSUPPORTED;
+    if (kernel_size < 1) return GDN_ERR_INVALID_ARG;
+    if (kernel_size > 4) return GDN_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return GDN_OK;
+    if (!x || !weight || !g || !beta || !state || !out) return GDN_ERR_INVALID_ARG;
+    if ((int64_t)num_seqs * num_v_heads > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+    // The two histories must not overlap: other workgroups still read rows of conv_state_in
+    // after one has written its new rows.
+    const int64_t C = (int64_t)(2 * num_qk_heads + num_v_heads) * d_k;
+    const int64_t hist_bytes = (int64_t)num_seqs * (kernel_size - 1) * C * (dtype == GDN_BF16 ? 2 : 4);
+    if (conv_state_in && conv_state_out && hist_bytes > 0) {
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(conv_state_in), b0 = reinterpret_cast<uintptr_t>(conv_state_out);
+        if (a0 < b0 + (uintptr_t)hist_bytes && b0 < a0 + (uintptr_t)hist_bytes) return GDN_ERR_INVALID_ARG;
+    }
+    gdn::DecodeArgs a;
+    a.q = a.k = a.v = nullptr;
+    a.g = g; a.beta = beta; a.state = state; a.out = out;
+    a.state_indices = nullptr; a.num_slots = 0;
+    a.num_seqs = num_seqs; a.num_qk_heads = num_qk_heads; a.num_v_heads = num_v_heads; a.d = d_k;
+    a.scale = scale; a.bf16 = (dtype == GDN_BF16);
+    a.qk_norm = (flags & GDN_FLAG_QK_L2NORM) != 0;
+    a.conv_x = x; a.conv_w = weight; a.conv_in = conv_state_in; a.conv_out = conv_state_out;
+    a.conv_K = kernel_size; a.conv_silu = (flags & GDN_FLAG_CONV_SILU) != 0;
+    return hip_status(gdn::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* gdn_status_string(gdn_status_t s) {
     switch (s) {
         case GDN_OK: return "GDN_OK";

@@ -37,12 +37,105 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTokBatch = 16;   // multi-token decode: tokens staged in LDS at a time
 
-template <int D, bool BF16, bool QKN>
+// Fused input prologue of the decode step (one token per sequence).
+struct DecodeConv {
+    const void* x;     // [N, C] raw q | k | v channels, C = (2 Hqk + Hv) D
+    const float* w;    // [C, K]
+    const void* hin;   // [N, K - 1, C] history (oldest first), or null (zeros)
+    void* hout;        // [N, K - 1, C] new history, or null; never overlaps hin
+    bool silu;
+};
+
+// The fused prologue of one workgroup: channel t < 3 D of its inputs (its QK
+// head's q, then k, then its V head's v channels), CPT channels per thread.
+// Its loads are issued before the state's (global loads complete in order, so
+// loads issued after the state's would wait for all of it).
+template <int D, bool BF16, int K, int NT>
+struct ConvPhase {
+    static constexpr int CPT = (3 * D + NT - 1) / NT;
+    static constexpr int KH = K > 1 ? K - 1 : 1;
+    uint32_t h[CPT][KH];   // history rows (input bits), oldest first
+    uint32_t x[CPT];       // the token
+    float w[CPT][K];       // taps
+    int64_t ch[CPT];       // channel index in the token row
+
+    __device__ __forceinline__ static uint32_t ld(const void* p, int64_t i) {
+        if constexpr (BF16) return reinterpret_cast<const uint16_t*>(p)[i];
+        else return __float_as_uint(reinterpret_cast<const float*>(p)[i]);
+    }
+    __device__ __forceinline__ static float widen(uint32_t r) {
+        if constexpr (BF16) return __uint_as_float(r << 16);
+        else return __uint_as_float(r);
+    }
+
+    __device__ __forceinline__ void load(const DecodeConv& cv, int n, int h_, int hq, int hqk, int hv, int tid) {
+        const int64_t C = (int64_t)(2 * hqk + hv) * D;
+        // Sequence n's history rows through a buffer resource: with no history its range is
+        // empty and every read returns 0, so the loads need no branch (a branch here made the
+        // wave wait for the first of them before issuing the rest).
+        constexpr int ES = BF16 ? 2 : 4;
+        const char* hbase = cv.hin ? reinterpret_cast<const char*>(cv.hin) + (int64_t)n * (K - 1) * C * ES
+                                   : reinterpret_cast<const char*>(cv.x);
+        const __amdgpu_buffer_rsrc_t hist = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(hbase), (short)0, cv.hin ? (int)((K - 1) * C * ES) : 0, 0x00020000);
+#pragma unroll
+        for (int r = 0; r < CPT; ++r) {
+            const int t = tid + r * NT;
+            const int tt = t < 3 * D ? t : 0;   // threads past the last channel load channel 0, store nothing
+            const int part = tt / D, j = tt % D;
+            ch[r] = part == 0 ? (int64_t)hq * D + j
+                    : part == 1 ? (int64_t)(hqk + hq) * D + j
+                                : (int64_t)2 * hqk * D + (int64_t)h_ * D + j;
+#pragma unroll
+            for (int i = 0; i < K - 1; ++i) {
+                const uint32_t off = (uint32_t)(((int64_t)i * C + ch[r]) * (BF16 ? 2 : 4));
+                if constexpr (BF16) h[r][i] = __builtin_amdgcn_raw_buffer_load_b16(hist, (int)off, 0, 0);
+                else h[r][i] = __builtin_amdgcn_raw_buffer_load_b32(hist, (int)off, 0, 0);
+            }
+            x[r] = ld(cv.x, (int64_t)n * C + ch[r]);
+#pragma unroll
+            for (int i = 0; i < K; ++i) w[r][i] = cv.w[ch[r] * K + i];
+        }
+    }
+
+    // y = sum_{i < K - 1} w[i] hist[i] + w[K - 1] x, optionally y * sigmoid(y), into s[t]; the
+    // channels' new history (old rows 1 .. K - 2, then the token) to hout, the q and k channels only
+    // by the first V head of their QK head, the one workgroup that owns them.
+    __device__ __forceinline__ void finish(const DecodeConv& cv, int n, int h_, int hqk, int hv, int tid,
+                                           float* __restrict__ s) const {
+        const int64_t C = (int64_t)(2 * hqk + hv) * D;
+        const bool owns_qk = (h_ % (hv / hqk)) == 0;
+#pragma unroll
+        for (int r = 0; r < CPT; ++r) {
+            const int t = tid + r * NT;
+            if (t >= 3 * D) break;
+            float y = 0.f;
+#pragma unroll
+            for (int i = 0; i < K - 1; ++i) y = fmaf(w[r][i], widen(h[r][i]), y);
+            y = fmaf(w[r][K - 1], widen(x[r]), y);
+            if (cv.silu) y = y * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(y * -1.4426950408889634f));
+            s[t] = y;
+            if (cv.hout && (t >= 2 * D || owns_qk)) {
+#pragma unroll
+                for (int i = 0; i < K - 1; ++i) {
+                    const uint32_t b = (i + 1 < K - 1) ? h[r][i + 1 < K - 1 ? i + 1 : 0] : x[r];
+                    const int64_t o = ((int64_t)n * (K - 1) + i) * C + ch[r];
+                    if constexpr (BF16) reinterpret_cast<uint16_t*>(cv.hout)[o] = (uint16_t)b;
+                    else reinterpret_cast<float*>(cv.hout)[o] = __uint_as_float(b);
+                }
+            }
+        }
+    }
+};
+
+// CK > 0: q, k and v come from the fused input prologue with K = CK taps (the
+// q, k, v pointers are unused); CK = 0: from the q, k, v arrays.
+template <int D, bool BF16, bool QKN, int CK = 0>
 __global__ __launch_bounds__(512) void decode_step_kernel(
     const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
     int32_t num_qk_heads, int32_t num_v_heads, float scale, void* __restrict__ out_,
-    const int32_t* __restrict__ state_indices, int32_t num_slots) {
+    const int32_t* __restrict__ state_indices, int32_t num_slots, DecodeConv cv) {
     constexpr int L = D / 16;                    // lanes per state row (16 floats each)
     constexpr int NT = (D * L < 512) ? D * L : 512;
     constexpr int ROWS_PER_PASS = NT / L;
@@ -73,7 +166,14 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
     }
     f32x4* S = reinterpret_cast<f32x4*>(state + (srow * num_v_heads + h) * (int64_t)D * D);
 
-    // Issue the state loads first: R rows x 4 float4 per thread.
+    // Fused prologue: its few loads go out ahead of the state's.
+    ConvPhase<D, BF16, (CK > 0 ? CK : 1), NT> cp;
+    if constexpr (CK > 0) {
+        cp.load(cv, n, h, hq, num_qk_heads, num_v_heads, tid);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // The state loads (first of all without the prologue): R rows x 4 float4 per thread.
     f32x4 s[R][4];
 #pragma unroll
     for (int m = 0; m < R; ++m) {
@@ -86,7 +186,18 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
     // Key / query slices owned by this lane: columns 4 * (c + L * i) .. +3.
     float kr[4][4], qr[4][4];
     const int64_t qk_base = ((int64_t)n * num_qk_heads + hq) * D;
-    if constexpr (BF16) {
+    __shared__ float s_qkv[CK > 0 ? 3 * D : 1];   // fused prologue: q, k, v of this workgroup
+    if constexpr (CK > 0) {
+        cp.finish(cv, n, h, num_qk_heads, num_v_heads, tid, s_qkv);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                qr[i][e] = s_qkv[4 * (c + L * i) + e];
+                kr[i][e] = s_qkv[D + 4 * (c + L * i) + e];
+            }
+    } else if constexpr (BF16) {
         const uint2* k2 = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(k_) + qk_base);
         const uint2* q2 = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(q_) + qk_base);
 #pragma unroll
@@ -147,7 +258,8 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
         a = group_sum<L>(a) * rk;
         bq = group_sum<L>(bq) * rq;
         float vi;
-        if constexpr (BF16) vi = bf16_bits_to_float(reinterpret_cast<const uint16_t*>(v_)[vo_base + row]);
+        if constexpr (CK > 0) vi = s_qkv[2 * D + row];
+        else if constexpr (BF16) vi = bf16_bits_to_float(reinterpret_cast<const uint16_t*>(v_)[vo_base + row]);
         else vi = reinterpret_cast<const float*>(v_)[vo_base + row];
         const float u = b * (vi - alpha * a);
         const float uk = u * rk;
@@ -360,22 +472,35 @@ hipError_t launch_decode_multi(const DecodeArgs& a, hipStream_t stream) {
     }
 }
 
-template <int D, bool BF16, bool QKN>
+template <int D, bool BF16, bool QKN, int CK>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     constexpr int L = D / 16;
     constexpr int NT = (D * L < 512) ? D * L : 512;
     const int64_t blocks = (int64_t)a.num_seqs * a.num_v_heads;
-    prof::begin(stream, "gdn_decode_step");
-    hipLaunchKernelGGL((decode_step_kernel<D, BF16, QKN>), dim3((unsigned)blocks), dim3(NT), 0, stream,
+    const DecodeConv cv{a.conv_x, a.conv_w, a.conv_in, a.conv_out, a.conv_silu};
+    prof::begin(stream, CK > 0 ? "gdn_decode_conv" : "gdn_decode_step");
+    hipLaunchKernelGGL((decode_step_kernel<D, BF16, QKN, CK>), dim3((unsigned)blocks), dim3(NT), 0, stream,
                        a.q, a.k, a.v, a.g, a.beta, a.state, a.num_qk_heads, a.num_v_heads, a.scale, a.out,
-                       a.state_indices, a.num_slots);
+                       a.state_indices, a.num_slots, cv);
     prof::end(stream);
     return hipGetLastError();
 }
 
+template <int D, bool BF16, int CK>
+static hipError_t launch_decode_c(const DecodeArgs& a, hipStream_t stream) {
+    return a.qk_norm ? launch_decode_t<D, BF16, true, CK>(a, stream) : launch_decode_t<D, BF16, false, CK>(a, stream);
+}
+
 template <int D, bool BF16>
 static hipError_t launch_decode_n(const DecodeArgs& a, hipStream_t stream) {
-    return a.qk_norm ? launch_decode_t<D, BF16, true>(a, stream) : launch_decode_t<D, BF16, false>(a, stream);
+    switch (a.conv_K) {
+        case 0: return launch_decode_c<D, BF16, 0>(a, stream);
+        case 1: return launch_decode_c<D, BF16, 1>(a, stream);
+        case 2: return launch_decode_c<D, BF16, 2>(a, stream);
+        case 3: return launch_decode_c<D, BF16, 3>(a, stream);
+        case 4: return launch_decode_c<D, BF16, 4>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

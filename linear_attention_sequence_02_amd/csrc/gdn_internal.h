@@ -27,6 +27,14 @@ struct DecodeArgs {
     int32_t num_seqs, num_qk_heads, num_v_heads, d;
     float scale;
     bool bf16;
+    // Fused input prologue (conv_K > 0): q, k, v come from the causal convolution of conv_x
+    // (one token per sequence) instead of the q, k, v arrays.
+    const void* conv_x = nullptr;   // [num_seqs, C]
+    const float* conv_w = nullptr;  // [C, conv_K]
+    const void* conv_in = nullptr;  // [num_seqs, conv_K - 1, C] or null (zeros)
+    void* conv_out = nullptr;       // [num_seqs, conv_K - 1, C] or null; never overlaps conv_in
+    int32_t conv_K = 0;
+    bool conv_silu = false;
 };
 
 struct PrefillArgs {

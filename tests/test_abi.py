@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
                                          "gdn_decode_multi", "gdn_prefill_ex", "gdn_decode_ex",
                                          "gdn_backward", "gdn_backward_workspace_size",
                                          "gdn_status_string", "gdn_build_info", "gdn_profile_start",
-                                         "gdn_profile_stop", "gdn_conv_prologue", "gdn_prefill_noalloc"}
+                                         "gdn_profile_stop", "gdn_conv_prologue", "gdn_prefill_noalloc",
+                                         "gdn_decode_conv"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -289,6 +290,41 @@ def test_conv_prologue_rejects(lib, over, status):
 
 def test_conv_prologue_with_no_sequences_is_a_no_op(lib):
     assert _conv(lib, n=0, T=0) == gdn.GDN_OK
+
+
+def _dconv(lib, **over):
+    a = dict(x=FAKE, w=FAKE, hin=None, hout=None, g=FAKE, b=FAKE, s=FAKE, n=2, hqk=16, hv=32, dk=128, dv=128, K=4,
+             scale=1.0, dt=gdn.GDN_BF16, flags=0, out=FAKE, stream=None)
+    a.update(over)
+    return lib.gdn_decode_conv(a["x"], a["w"], a["hin"], a["hout"], a["g"], a["b"], a["s"], a["n"], a["hqk"],
+                               a["hv"], a["dk"], a["dv"], a["K"], a["scale"], a["dt"], a["flags"], a["out"],
+                               a["stream"])
+
+
+# History of 2 sequences x 3 rows x 8192 channels x 2 bytes = 98,304 bytes.
+@pytest.mark.parametrize("over,status", [
+    (dict(x=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(w=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(s=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(out=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(K=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(K=5), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dk=100, dv=100), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(hqk=3), gdn.GDN_ERR_INVALID_ARG),
+    (dict(flags=0x4), gdn.GDN_ERR_INVALID_ARG),
+    (dict(hin=ctypes.c_void_p(0x100000), hout=ctypes.c_void_p(0x100000)), gdn.GDN_ERR_INVALID_ARG),
+    (dict(hin=ctypes.c_void_p(0x100000), hout=ctypes.c_void_p(0x100000 + 98303)), gdn.GDN_ERR_INVALID_ARG),
+    (dict(hin=ctypes.c_void_p(0x100000 + 98303), hout=ctypes.c_void_p(0x100000)), gdn.GDN_ERR_INVALID_ARG),
+])
+def test_decode_conv_rejects(lib, over, status):
+    assert _dconv(lib, **over) == status
+
+
+def test_decode_conv_with_no_sequences_is_a_no_op(lib):
+    assert _dconv(lib, n=0) == gdn.GDN_OK
+    # histories that merely touch (one ends where the other starts) do not overlap; with no
+    # sequences nothing is enqueued either way
+    assert _dconv(lib, n=0, hin=ctypes.c_void_p(0x100000), hout=ctypes.c_void_p(0x100000 + 98304)) == gdn.GDN_OK
 
 
 def test_noalloc_rejects_sizes_beyond_its_array(lib):

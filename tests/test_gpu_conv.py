@@ -135,3 +135,85 @@ def test_conv_then_prefill_then_decode():
     eo, ef = rel_l2(got, ro), rel_l2(state.cpu().numpy(), rf)
     log(f"[parity] conv+prefill+decode: out {eo:.3e} state {ef:.3e}")
     assert eo <= 1e-2 and ef <= 1e-2
+
+
+@pytest.mark.parametrize("dtype,d,K,silu,norm,history,scale", [
+    ("bf16", 128, 4, True, True, True, 1.0), ("bf16", 128, 4, False, False, False, 1.0),
+    ("bf16", 128, 2, True, True, True, 128 ** -0.5), ("fp32", 32, 3, True, True, True, 1.0),
+    ("fp32", 16, 4, False, True, False, 0.25), ("fp32", 64, 1, True, False, True, 1.0)])
+def test_decode_conv_step(dtype, d, K, silu, norm, history, scale):
+    """gdn_decode_conv (prologue fused into the decode step) against the oracle's prologue followed
+    by one step of its recurrence from the same state; the new history bit for bit."""
+    N, hqk, hv = 5, 2, 4
+    c = I.conv_inputs(lengths=[1] * N, hqk=hqk, hv=hv, d=d, K=K, dtype=dtype, seed=340 + d + K, history=history,
+                      name=f"decode_conv_{dtype}_d{d}_K{K}")
+    gb = I.draw(lengths=[1] * N, hqk=hqk, hv=hv, dk=d, dtype=dtype, seed=341 + d)
+    s0 = I.large_state(N, hv, d, seed=342, std=0.1)
+    state = torch.from_numpy(s0.copy()).cuda()
+    hist = _dev(c.history, dtype) if history else None
+    hout = torch.full((N, K - 1, c.x.shape[1]), 7.0, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                      device="cuda")
+    log(f"[gpu] gdn_decode_conv {c.name} silu={silu} norm={norm} history={history}")
+    out, h2 = gdn.gdn_decode_conv(_dev(c.x, dtype), torch.from_numpy(c.w).cuda(), torch.from_numpy(gb.g).cuda(),
+                                  torch.from_numpy(gb.beta).cuda(), state, hist, num_qk_heads=hqk, num_v_heads=hv,
+                                  conv_state_out=hout, silu=silu, qk_l2norm=norm, scale=scale)
+    torch.cuda.synchronize()
+    assert h2.data_ptr() == hout.data_ptr()
+    rq, rk, rv, rh = oracle.conv_prologue(c.x, c.w, hqk, hv, d, d, c.cu_seqlens, c.history, silu_act=silu,
+                                          qk_l2norm=norm)
+    ro, rf = oracle.recurrent(rq, rk, rv, gb.g.astype(np.float64), gb.beta.astype(np.float64), s0, c.cu_seqlens,
+                              scale=scale)
+    eo, es = rel_l2(_f64(out), ro), rel_l2(state.cpu().numpy(), rf)
+    log(f"[parity] {c.name}: out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    if K > 1:
+        if dtype == "bf16":
+            assert np.array_equal(hout.view(torch.int16).cpu().numpy().view(np.uint16),
+                                  I.f32_to_bf16_bits(rh.astype(np.float32)))
+        else:
+            assert np.array_equal(hout.cpu().numpy().astype(np.float64), rh)
+
+
+def test_conv_then_prefill_then_fused_decode():
+    """The unfused prologue and the prefill over 3 sequences, then 3 fused decode steps per sequence
+    alternating two history arrays, against the oracle run on the whole sequences."""
+    hqk, hv, d, K = 2, 4, 128, 4
+    lengths = [70, 129, 5]
+    steps = 3
+    N = len(lengths)
+    total = [L + steps for L in lengths]
+    c = I.conv_inputs(lengths=total, hqk=hqk, hv=hv, d=d, K=K, dtype="bf16", seed=350, history=False,
+                      name="conv_prefill_fused_decode")
+    gb = I.draw(lengths=total, hqk=hqk, hv=hv, dk=d, dtype="bf16", seed=351)
+    cu_all = c.cu_seqlens
+    pre_rows = np.concatenate([np.arange(cu_all[n], cu_all[n] + lengths[n]) for n in range(N)])
+    cu_pre = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    w = torch.from_numpy(c.w).cuda()
+    log("[gpu] conv prologue + prefill, then fused decode")
+    q, k, v, hist = gdn.gdn_conv_prologue(_dev(c.x[pre_rows], "bf16"), w, None, torch.from_numpy(cu_pre).cuda(),
+                                          num_qk_heads=hqk, num_v_heads=hv, silu=True, qk_l2norm=True,
+                                          conv_state_out=True)
+    out_pre, state = gdn.gdn_prefill(q, k, v, torch.from_numpy(gb.g[pre_rows]).cuda(),
+                                     torch.from_numpy(gb.beta[pre_rows]).cuda(), None,
+                                     torch.from_numpy(cu_pre).cuda())
+    spare = torch.empty_like(hist)
+    outs = []
+    for s in range(steps):
+        rows = np.array([cu_all[n] + lengths[n] + s for n in range(N)])
+        o, _ = gdn.gdn_decode_conv(_dev(c.x[rows], "bf16"), w, torch.from_numpy(gb.g[rows]).cuda(),
+                                   torch.from_numpy(gb.beta[rows]).cuda(), state, hist, num_qk_heads=hqk,
+                                   num_v_heads=hv, conv_state_out=spare, silu=True, qk_l2norm=True)
+        outs.append(o)
+        hist, spare = spare, hist
+    torch.cuda.synchronize()
+    rq, rk, rv, rh = oracle.conv_prologue(c.x, c.w, hqk, hv, d, d, cu_all, None, silu_act=True, qk_l2norm=True)
+    ro, rf = oracle.recurrent(rq, rk, rv, gb.g.astype(np.float64), gb.beta.astype(np.float64), None, cu_all)
+    got = np.zeros_like(ro)
+    got[pre_rows] = _f64(out_pre)
+    for s in range(steps):
+        got[[cu_all[n] + lengths[n] + s for n in range(N)]] = _f64(outs[s])
+    eo, ef = rel_l2(got, ro), rel_l2(state.cpu().numpy(), rf)
+    log(f"[parity] conv+prefill+fused decode: out {eo:.3e} state {ef:.3e}")
+    assert eo <= 1e-2 and ef <= 1e-2
+    assert np.array_equal(hist.view(torch.int16).cpu().numpy().view(np.uint16),
+                          I.f32_to_bf16_bits(rh.astype(np.float32)))
