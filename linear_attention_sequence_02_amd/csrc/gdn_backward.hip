@@ -284,6 +284,10 @@ __device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, cons
                                           float* __restrict__ ck, int64_t b) {
     using Sh = ScanShape<D>;
     constexpr int NTD = Sh::NTD, TPW = Sh::TPW, EPT = Sh::EPT;
+    // Every wave has TPW whole d tiles when the tiles divide evenly among the four waves; the
+    // guard below is then a constant (left to the wave index, it put a branch around every
+    // tile's products and kept their LDS reads from being batched).
+    constexpr bool kAllTiles = (NTD % 4 == 0);
     constexpr bool rev = REV;
     auto& Kc = sm.Kc;
     auto& Qc = sm.Qc;
@@ -360,7 +364,7 @@ __device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, cons
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int tk = w + 4 * i;
-            acc[i] = (src && tk < NTD) ? *reinterpret_cast<const f32x4*>(src + row * D + 16 * tk + 4 * g4)
+            acc[i] = (src && (kAllTiles || tk < NTD)) ? *reinterpret_cast<const f32x4*>(src + row * D + 16 * tk + 4 * g4)
                                        : f32x4{0.f, 0.f, 0.f, 0.f};
         }
         // Let these loads finish here, once: otherwise the compiler, unable to
@@ -383,100 +387,163 @@ __device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, cons
     mf::lds_barrier();
     if (nint > 2) fetch(pa, 2);
     if (nint > 3) fetch(pb, 3);
+    f32x4 zkeep = {0.f, 0.f, 0.f, 0.f};   // reverse: this chunk's Z
+    // Each phase below reads all of its LDS operands before its products (a scheduling barrier
+    // between the two): left to the scheduler, every product waited for its own operand reads.
     auto chunk = [&](int q, Pre& pre) {
         const int c = chunk_at(q), bb = q % 3, pp = q & 1;
-        // Checkpoint: the state at the chunk's start (forward), the gradient at its end (reverse).
-        float* dst = ck + ((cbase + c) * hv + h) * (int64_t)D * D + row * D;
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int tk = w + 4 * i;
-            if (tk < NTD) *reinterpret_cast<f32x4*>(dst + 16 * tk + 4 * g4) = acc[i];
-        }
-        // This wave's share of K X^T (X: the state or its gradient).
+        // This wave's share of K X^T (X: the state or its gradient) and, in reverse, Z = P^T dO
+        // (no dependence on the gradient).
         {
+            float ka[TPW][4];
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int tk = w + 4 * i;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ka[i][e] = (kAllTiles || tk < NTD) ? Kc[bb][m][16 * tk + 4 * g4 + e] : 0.f;
+            }
+            float pz[4], xz[4];
+            if constexpr (REV) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    pz[kk] = Pc[bb][4 * kk + g4][m];
+                    xz[kk] = Xc[bb][4 * kk + g4][m];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 ps = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
                 const int tk = w + 4 * i;
-                if (tk < NTD) {
+                if (kAllTiles || tk < NTD) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) ps = mfma4(Kc[bb][m][16 * tk + 4 * g4 + e], acc[i][e], ps);
+                    for (int e = 0; e < 4; ++e) ps = mfma4(ka[i][e], acc[i][e], ps);
                 }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) part[pp][w][4 * g4 + e][m] = ps[e];
-        }
-        // Reverse: Z = P^T dO (no dependence on the gradient).
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (REV) {
+            if constexpr (REV) {
+                f32x4 zz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) z = mfma4(Pc[bb][4 * kk + g4][m], Xc[bb][4 * kk + g4][m], z);
+                for (int kk = 0; kk < 4; ++kk) zz = mfma4(pz[kk], xz[kk], zz);
+                zkeep = zz;
+            }
         }
         mf::lds_barrier();
         // Buffer (q + 2) % 3 was last read in chunk q - 1, which every wave has finished.
         if (q + 2 < nint) commit(pre, (q + 2) % 3);
-        if (q + 4 < nint) fetch(pre, q + 4);
-        const float GL = Gc[bb][kC - 1];   // exp(gamma_last)
-        if constexpr (!REV) {
-            // U = T diag(beta) (V - diag(Gam) K S0^T), then Gp U to this wave's LDS rows.
-            f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int tau = 4 * kk + g4;
-                const float ks = part[pp][0][tau][m] + part[pp][1][tau][m] + part[pp][2][tau][m] + part[pp][3][tau][m];
-                const float xv = bc[bb][tau] * (Xc[bb][tau][m] - Gc[bb][tau] * ks);
-                u = mfma4(Tc[bb][m][tau], xv, u);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tau = 4 * g4 + e;
-                Uw[w][tau][m] = Hc[bb][tau] * u[e];
-            }
-            wave_lds_sync();
-            // S^T <- exp(gamma_last) S^T + K^T (Gp U)
+        // Checkpoint: the state at the chunk's start (forward), the gradient at its end (reverse),
+        // unchanged until the update below. Stored after the commit: stores count among the
+        // outstanding vector memory operations, and the commit's wait for its loads (issued two
+        // chunks earlier) would otherwise also wait for these stores to complete.
+        {
+            float* dst = ck + ((cbase + c) * hv + h) * (int64_t)D * D + row * D;
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
                 const int tk = w + 4 * i;
-                if (tk < NTD) {
+                if (kAllTiles || tk < NTD) *reinterpret_cast<f32x4*>(dst + 16 * tk + 4 * g4) = acc[i];
+            }
+        }
+        if (q + 4 < nint) fetch(pre, q + 4);
+        const float GL = Gc[bb][kC - 1];   // exp(gamma_last)
+        // The update's K (and Q) operands, read with the phase's other operands.
+        float ku[TPW][4], qu[TPW][4];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int tk = w + 4 * i;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int tau = 4 * kk + g4;
+                ku[i][kk] = (kAllTiles || tk < NTD) ? Kc[bb][tau][16 * tk + m] : 0.f;
+                if constexpr (REV) qu[i][kk] = (kAllTiles || tk < NTD) ? Qc[bb][tau][16 * tk + m] : 0.f;
+            }
+        }
+        if constexpr (!REV) {
+            // U = T diag(beta) (V - diag(Gam) K S0^T), then Gp U to this wave's LDS rows.
+            float pr[4][4], xr[4], gr[4], br[4], tr[4], hr[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int tau = 4 * kk + g4;
+#pragma unroll
+                for (int ww = 0; ww < 4; ++ww) pr[kk][ww] = part[pp][ww][tau][m];
+                xr[kk] = Xc[bb][tau][m];
+                gr[kk] = Gc[bb][tau];
+                br[kk] = bc[bb][tau];
+                tr[kk] = Tc[bb][m][tau];
+                hr[kk] = Hc[bb][4 * g4 + kk];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const float ks = (pr[kk][0] + pr[kk][1]) + (pr[kk][2] + pr[kk][3]);
+                u = mfma4(tr[kk], br[kk] * (xr[kk] - gr[kk] * ks), u);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Uw[w][4 * g4 + e][m] = hr[e] * u[e];
+            wave_lds_sync();
+            // S^T <- exp(gamma_last) S^T + K^T (Gp U)
+            float uu[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) uu[kk] = Uw[w][4 * kk + g4][m];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int tk = w + 4 * i;
+                if (kAllTiles || tk < NTD) {
                     f32x4 a = acc[i] * GL;
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        const int tau = 4 * kk + g4;
-                        a = mfma4(Kc[bb][tau][16 * tk + m], Uw[w][tau][m], a);
-                    }
+                    for (int kk = 0; kk < 4; ++kk) a = mfma4(ku[i][kk], uu[kk], a);
                     acc[i] = a;
                 }
             }
         } else {
             // Y = Gp K G^T + scale Z, dU = T^T Y, then -Gam beta dU to this wave's LDS rows.
+            float pr[4][4], hr[4], gr[4], br[4], tt[4], gx[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tau = 4 * g4 + e;
-                const float kg = part[pp][0][tau][m] + part[pp][1][tau][m] + part[pp][2][tau][m] + part[pp][3][tau][m];
-                Uw[w][tau][m] = fmaf(Hc[bb][tau], kg, scale * z[e]);
+#pragma unroll
+                for (int ww = 0; ww < 4; ++ww) pr[e][ww] = part[pp][ww][tau][m];
+                hr[e] = Hc[bb][tau];
+                gr[e] = Gc[bb][tau];
+                br[e] = bc[bb][tau];
+                const int tk4 = 4 * e + g4;   // reduction index of the products below
+                tt[e] = Tc[bb][tk4][m];
+                gx[e] = scale * Gc[bb][tk4] * Xc[bb][tk4][m];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float kg = (pr[e][0] + pr[e][1]) + (pr[e][2] + pr[e][3]);
+                Uw[w][4 * g4 + e][m] = fmaf(hr[e], kg, scale * zkeep[e]);
             }
             wave_lds_sync();
+            float y[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) y[kk] = Uw[w][4 * kk + g4][m];
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 du = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) du = mfma4(Tc[bb][4 * kk + g4][m], Uw[w][4 * kk + g4][m], du);
+            for (int kk = 0; kk < 4; ++kk) du = mfma4(tt[kk], y[kk], du);
             wave_lds_sync();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tau = 4 * g4 + e;
-                Uw[w][tau][m] = -Gc[bb][tau] * bc[bb][tau] * du[e];
-            }
+            for (int e = 0; e < 4; ++e) Uw[w][4 * g4 + e][m] = -gr[e] * br[e] * du[e];
             wave_lds_sync();
             // G^T <- exp(gamma_last) G^T + Q^T (scale Gam dO) + K^T (-Gam beta dU)
+            float uu[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) uu[kk] = Uw[w][4 * kk + g4][m];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
                 const int tk = w + 4 * i;
-                if (tk < NTD) {
+                if (kAllTiles || tk < NTD) {
                     f32x4 a = acc[i] * GL;
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
-                        const int tau = 4 * kk + g4;
-                        a = mfma4(Qc[bb][tau][16 * tk + m], scale * Gc[bb][tau] * Xc[bb][tau][m], a);
-                        a = mfma4(Kc[bb][tau][16 * tk + m], Uw[w][tau][m], a);
+                        a = mfma4(qu[i][kk], gx[kk], a);
+                        a = mfma4(ku[i][kk], uu[kk], a);
                     }
                     acc[i] = a;
                 }
@@ -491,7 +558,7 @@ __device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, cons
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int tk = w + 4 * i;
-            if (tk < NTD) *reinterpret_cast<f32x4*>(dinit + sbase + row * D + 16 * tk + 4 * g4) = acc[i];
+            if (kAllTiles || tk < NTD) *reinterpret_cast<f32x4*>(dinit + sbase + row * D + 16 * tk + 4 * g4) = acc[i];
         }
     }
 }
