@@ -24,7 +24,11 @@ Roofline figures use algorithmic work only:
       tokens/s, the whole-call MFMA fraction and the longest launch's own
       fraction over the tokens it produces. They run before the headline
       workload (whose input is made resident first), each after 0.3 s of
-      warm-up calls, so the headline's steps start on a busy GPU.
+      warm-up calls. The headline itself runs 0.5 s of untimed calls before
+      its W warm-up steps: after the idle gap that follows the configs, the
+      first calls ran about 8% slower while the clock settled (0.948 against
+      0.875 ms per step with W = 5), so the timed steps measure the steady
+      state whatever W is.
   decode: 1,080,098,816 bytes per step for 256 sequences (state read + write
       plus q, k, v, g, beta, out); also on a state pool addressed by slot
       ("decode.slots": 256 of 384 rows in seeded random order, and
@@ -96,7 +100,9 @@ PEAK_FP32_MFMA_TFLOPS = 157.3
 BACKWARD_FLOP_PER_TOKEN = 17 * 128 * 128 * 32
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"gdn_segment_out": "gdn_segment.hip", "gdn_segment_maps": "gdn_segment.hip",
-                  "gdn_decode_step": "gdn_decode.hip", "gdn_decode_multi": "gdn_decode.hip"}
+                  "gdn_segment_combine": "gdn_segment.hip",
+                  "gdn_decode_step": "gdn_decode.hip", "gdn_decode_multi": "gdn_decode.hip",
+                  "gdn_decode_conv": "gdn_decode.hip", "gdn_conv_prologue": "gdn_conv.hip"}
 
 
 def decode_bytes(n, hqk=16, hv=32, d=128, tokens=1):
@@ -448,10 +454,10 @@ def main():
         print(json.dumps({"config": args.config, **configs[args.config]}), flush=True)
         return
 
-    log(f"[bench] prefill: {args.warmup} warmup + {args.steps} timed steps")
+    log(f"[bench] prefill: 0.5 s of warm-up calls, {args.warmup} warmup + {args.steps} timed steps")
     each = []
     rec, (d, out, fin, ws, prefill) = prefill_record(gdn, torch, x, dev, args.steps, args.warmup, per_step=each,
-                                                     prepared=head)
+                                                     prepared=head, warm_s=0.5)
     ms = rec["ms_per_step"]
     kern = rec["kernels_ms_per_launch"]
     tokens_per_s = x.T / (ms / 1e3)
@@ -653,7 +659,8 @@ def main():
                                    "kernels_ms_per_launch": {k_: v_[1] for k_, v_ in ckern.items()},
                                    "bytes_per_launch": cbytes, "tokens_per_s": T / (cms / 1e3),
                                    "roofline": {"kernel": "gdn_conv_prologue", "bound": "hbm", "achieved": cgbs,
-                                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": cgbs / PEAK_HBM_GBS}}
+                                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": cgbs / PEAK_HBM_GBS,
+                                                "traffic": recorded_traffic("gdn_conv_prologue", cx.name)}}
         log(f"[bench] conv prologue {cms:.3f} ms/step, {cgbs:.1f} GB/s")
         del xc, wc, qc, kc_, vc, hc
         # Decode with the prologue: 256 sequences, one token each, history and state carried in place.
@@ -698,7 +705,8 @@ def main():
             "workload": cd.name, "ms_per_step": fms_, "tokens_per_s": n / (fms_ / 1e3), "kernel_ms_per_launch": fkms,
             "bytes_per_launch": fbytes,
             "roofline": {"kernel": "gdn_decode_conv", "bound": "hbm", "achieved": fgbs, "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": fgbs / PEAK_HBM_GBS}}
+                         "unit": "GB/s", "frac": fgbs / PEAK_HBM_GBS,
+                         "traffic": recorded_traffic("gdn_decode_conv", cd.name)}}
         log(f"[bench] fused decode with the prologue {fms_:.3f} ms/step, {fgbs:.1f} GB/s")
         del dd_, xd, hd, hd2, hist_pair, wd, st, qd, kd, vd, od
         torch.cuda.empty_cache()
