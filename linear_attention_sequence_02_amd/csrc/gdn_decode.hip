@@ -118,7 +118,9 @@ struct ConvPhase {
             if (cv.hout && (t >= 2 * D || owns_qk)) {
 #pragma unroll
                 for (int i = 0; i < K - 1; ++i) {
-                    const uint32_t b = (i + 1 < K - 1) ? h[r][i + 1 < K - 1 ? i + 1 : 0] : x[r];
+                    // new row i: old row i + 1, the last one the token ((i + 1) % KH only keeps the
+                    // unused branch's index in range)
+                    const uint32_t b = (i == K - 2) ? x[r] : h[r][(i + 1) % KH];
                     const int64_t o = ((int64_t)n * (K - 1) + i) * C + ch[r];
                     if constexpr (BF16) reinterpret_cast<uint16_t*>(cv.hout)[o] = (uint16_t)b;
                     else reinterpret_cast<float*>(cv.hout)[o] = __uint_as_float(b);
