@@ -20,9 +20,11 @@ Roofline figures use algorithmic work only:
       produces (all but each sequence's first segment, whose length comes from
       gdn_prefill_segment_chunks).
   configs ("configs"): the same record for the 4,096-token layer, the
-      8-sequence varlen batch and the 262,144-token long context, each with
-      tokens/s, the whole-call MFMA fraction and the longest launch's own
-      fraction over the tokens it produces. They run before the headline
+      8-sequence varlen batch, the 262,144-token long context and one GPU's
+      share of the 65,536-token layer under tensor parallelism 4 (4 QK / 8 V
+      heads), each with tokens/s, the whole-call MFMA fraction (over the timed
+      step, at the algorithmic work of its own head counts) and the longest
+      launch's own fraction over the tokens it produces. They run before the headline
       workload (whose input is made resident first), each after 0.3 s of
       warm-up calls. The headline itself runs 0.5 s of untimed calls before
       its W warm-up steps: after the idle gap that follows the configs, the
@@ -103,6 +105,16 @@ KERNEL_SOURCES = {"gdn_segment_out": "gdn_segment.hip", "gdn_segment_maps": "gdn
                   "gdn_segment_combine": "gdn_segment.hip",
                   "gdn_decode_step": "gdn_decode.hip", "gdn_decode_multi": "gdn_decode.hip",
                   "gdn_decode_conv": "gdn_decode.hip", "gdn_conv_prologue": "gdn_conv.hip"}
+
+
+def prefill_work_per_token(hqk=16, hv=32, d=128, chunk=64):
+    """Algorithmic flop and HBM bytes per token of the chunked prefill: per QK head the two
+    lower-triangular Gram products (chunk d each), per V head T K, T V and P U (chunk d each) and
+    W S^T, Q S^T, U^T K (2 d^2 each); bytes: q, k, v, out in bf16, g and beta in fp32. The layer's
+    16 / 32 heads give PREFILL_FLOP_PER_TOKEN and PREFILL_BYTES_PER_TOKEN."""
+    flop = hqk * 2 * chunk * d + hv * (3 * chunk * d + 6 * d * d)
+    nbytes = 2 * hqk * d * 2 + 2 * hv * d * 2 + 2 * hv * 4
+    return flop, nbytes
 
 
 def decode_bytes(n, hqk=16, hv=32, d=128, tokens=1):
@@ -358,9 +370,9 @@ def warm(fn, seconds, torch):
 
 def prefill_record(gdn, torch, x, dev, steps, warmup, per_step=None, prepared=None, warm_s=0.0):
     """Time gdn_prefill on one input set (resident in HBM, workspace preallocated): tokens/s of the
-    whole call, its MFMA fraction (algorithmic flop over the sum of the launches' mean durations),
-    and the longest launch's own fraction over the tokens whose outputs it produces. warm_s: run the
-    call for that long before the `warmup` steps."""
+    whole call, its MFMA and HBM fractions (algorithmic work of the input's head counts over the
+    timed step), and the longest launch's own fraction over the tokens whose outputs it produces.
+    warm_s: run the call for that long before the `warmup` steps."""
     d, out, fin, ws, call = prepared if prepared is not None else prefill_prepare(gdn, torch, x, dev)
     if warm_s > 0:
         warm(call, warm_s, torch)
@@ -368,22 +380,23 @@ def prefill_record(gdn, torch, x, dev, steps, warmup, per_step=None, prepared=No
     seg_chunks = gdn.gdn_prefill_segment_chunks(x.T, x.num_seqs, x.hqk, x.hv, x.dk, x.dv, gdn.GDN_BF16)
     per_launch = {k_: v_[1] for k_, v_ in kern.items()}
     call_ms = sum(per_launch.values()) if per_launch else ms
-    flop = PREFILL_FLOP_PER_TOKEN * x.T
+    fpt, bpt = prefill_work_per_token(x.hqk, x.hv, x.dk)
+    flop = fpt * x.T
     tokens = launch_tokens(x, seg_chunks)
     longest = max(per_launch, key=per_launch.get) if per_launch else None
     rec = {
         "workload": x.name, "tokens": x.T, "num_seqs": x.num_seqs, "ms_per_step": ms, "steps": steps,
         "warmup": warmup, "tokens_per_s": x.T / (ms / 1e3),
         "frac_mfma_peak_whole_call": flop / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-        "frac_hbm_peak_whole_call": PREFILL_BYTES_PER_TOKEN * x.T / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        "frac_hbm_peak_whole_call": bpt * x.T / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+        "num_qk_heads": x.hqk, "num_v_heads": x.hv, "flop_per_token": fpt,
         "kernels_ms_per_launch": per_launch, "launches_ms_sum": call_ms, "segment_chunks": seg_chunks,
         "tokens_per_launch": tokens,
     }
     if longest is not None:
         lt = tokens.get(longest, 0)
         rec["longest_launch"] = {"kernel": longest, "ms_per_launch": per_launch[longest], "tokens": lt,
-                                 "frac_mfma_peak": PREFILL_FLOP_PER_TOKEN * lt / (per_launch[longest] / 1e3) / 1e12
-                                 / PEAK_BF16_TFLOPS}
+                                 "frac_mfma_peak": fpt * lt / (per_launch[longest] / 1e3) / 1e12 / PEAK_BF16_TFLOPS}
     return rec, (d, out, fin, ws, call)
 
 
@@ -401,7 +414,8 @@ def main():
     ap.add_argument("--no-conv", action="store_true", help="skip the input prologue records")
     ap.add_argument("--config", default=None,
                     help="time only this prefill configuration and print its record (for profiling): one of "
-                         "qwen3next_gdn_prefill_T4096, qwen3next_gdn_varlen8, qwen3next_gdn_long_T262144")
+                         "qwen3next_gdn_prefill_T4096, qwen3next_gdn_varlen8, qwen3next_gdn_long_T262144, "
+                         "qwen3next_gdn_prefill_T65536_tp4_share")
     ap.add_argument("--no-peaks", action="store_true", help="skip the HBM / MFMA microbenchmarks")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one 256 MiB device-to-device copy (for scaling rocprofv3 byte counters)")
@@ -430,7 +444,8 @@ def main():
     configs = {}
     table = (("qwen3next_gdn_prefill_T4096", lambda: I.qwen3_next_prefill(T=4096), args.steps),
              ("qwen3next_gdn_varlen8", I.varlen_prefill, args.steps),
-             ("qwen3next_gdn_long_T262144", I.long_context, max(3, args.steps // 4)))
+             ("qwen3next_gdn_long_T262144", I.long_context, max(3, args.steps // 4)),
+             ("qwen3next_gdn_prefill_T65536_tp4_share", I.tp_share_prefill, args.steps))
     if args.config is not None:
         table = tuple(t_ for t_ in table if t_[0] == args.config)
         if not table:

@@ -259,6 +259,13 @@ def qwen3_next_prefill(T: int = 4096, dtype: str = "bf16", seed: int | None = No
                 seed=seed, scale=scale, name=f"qwen3next_gdn_prefill_T{T}")
 
 
+def tp_share_prefill(T: int = 65536, tp: int = 4, dtype: str = "bf16", seed: int = 1008) -> GdnInputs:
+    """One GPU's share of the layer under tensor parallelism of degree tp: the QK heads and their V
+    heads split evenly (16/tp QK, 32/tp V heads), the full sequence, the layer's distributions."""
+    return draw(T=T, hqk=QWEN3_NEXT_HQK // tp, hv=QWEN3_NEXT_HV // tp, dk=QWEN3_NEXT_D, dtype=dtype,
+                seed=seed, name=f"qwen3next_gdn_prefill_T{T}_tp{tp}_share")
+
+
 def varlen_prefill(dtype: str = "bf16", seed: int = 1002) -> GdnInputs:
     """8 packed sequences, lengths uniform in [1024, 16384], chunk-padded total <= 65536,
     initial states 0.01 * N(0, 1)."""

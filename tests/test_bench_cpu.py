@@ -21,6 +21,13 @@ def test_prefill_flop_per_token():
     assert bench.PREFILL_FLOP_PER_TOKEN == HQK * per_qk + HV * per_v == 4_194_304
 
 
+def test_prefill_work_follows_the_head_counts():
+    assert bench.prefill_work_per_token(16, 32, 128) == (bench.PREFILL_FLOP_PER_TOKEN, bench.PREFILL_BYTES_PER_TOKEN)
+    # one GPU's share under tensor parallelism 4 does a quarter of the layer's work per token
+    f4, b4 = bench.prefill_work_per_token(4, 8, 128)
+    assert 4 * f4 == bench.PREFILL_FLOP_PER_TOKEN and 4 * b4 == bench.PREFILL_BYTES_PER_TOKEN
+
+
 def test_prefill_bytes_per_token():
     # q, k (bf16, per QK head), v and out (bf16, per V head), g and beta (fp32, per V head)
     assert bench.PREFILL_BYTES_PER_TOKEN == 2 * HQK * D * 2 + 2 * HV * D * 2 + 2 * HV * 4 == 24_832

@@ -200,6 +200,14 @@ def test_prefill_bf16_qwen_layer_T65536():
     _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
 
 
+def test_prefill_bf16_tp4_share():
+    # One GPU's share at tensor parallelism 4 (4 QK / 8 V heads, the full 65,536 tokens): with
+    # fewer heads the segment rule picks 32-chunk segments, 33 per head.
+    x = I.tp_share_prefill()
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_BF16, TOL_BF16_SLICE)
+
+
 def test_prefill_bf16_varlen8():
     x = I.varlen_prefill()
     out, fin = run_prefill(x)
