@@ -129,13 +129,16 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_calls(fn, steps, warmup, torch, profile=True, per_step=None):
+def time_calls(fn, steps, warmup, torch, profile=True, per_step=None, warm_s=0.0):
     """Mean ms per call over `steps` back-to-back calls, HIP events on the current stream around the
     whole run and nothing else inside it (this is the number `value` comes from). If `profile`, a
     second run of `steps` calls with the library's per-launch HIP events on gives each kernel's mean
     launch time (the roofline's figure). If `per_step` is a list, a third run brackets each call with
-    its own events and appends the per-call times (median and min)."""
+    its own events and appends the per-call times (median and min). `warm_s`: run the call for that
+    long before the `warmup` calls (clocks settle after lighter work)."""
     import linear_attention_sequence_02_amd as gdn
+    if warm_s > 0:
+        warm(fn, warm_s, torch)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -374,9 +377,7 @@ def prefill_record(gdn, torch, x, dev, steps, warmup, per_step=None, prepared=No
     timed step), and the longest launch's own fraction over the tokens whose outputs it produces.
     warm_s: run the call for that long before the `warmup` steps."""
     d, out, fin, ws, call = prepared if prepared is not None else prefill_prepare(gdn, torch, x, dev)
-    if warm_s > 0:
-        warm(call, warm_s, torch)
-    ms, kern = time_calls(call, steps, warmup, torch, per_step=per_step)
+    ms, kern = time_calls(call, steps, warmup, torch, per_step=per_step, warm_s=warm_s)
     seg_chunks = gdn.gdn_prefill_segment_chunks(x.T, x.num_seqs, x.hqk, x.hv, x.dk, x.dv, gdn.GDN_BF16)
     per_launch = {k_: v_[1] for k_, v_ in kern.items()}
     call_ms = sum(per_launch.values()) if per_launch else ms
@@ -552,7 +553,7 @@ def main():
         def decode():
             gdn.gdn_decode_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], state, out=dout)
 
-        dms, dkern = time_calls(decode, args.steps, args.warmup, torch)
+        dms, dkern = time_calls(decode, args.steps, args.warmup, torch, warm_s=0.2)
         kms = dkern.get("gdn_decode_step", (0, dms))[1]
         nbytes = decode_bytes(n)
         gbs = nbytes / (kms / 1e3) / 1e9
@@ -574,7 +575,7 @@ def main():
         def decode_slots():
             gdn.gdn_decode_step_slots(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], pool, idx, out=dout)
 
-        sms, skern = time_calls(decode_slots, args.steps, args.warmup, torch)
+        sms, skern = time_calls(decode_slots, args.steps, args.warmup, torch, warm_s=0.2)
         skms = skern.get("gdn_decode_step", (0, sms))[1]
         # The same 256 rows with sequence n on the n-th lowest of them: rows in ascending order.
         idx_sorted = torch.sort(idx).values.contiguous()
@@ -584,7 +585,7 @@ def main():
         def decode_slots_sorted():
             gdn.gdn_decode_step_slots(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], pool_s, idx_sorted, out=dout)
 
-        oms, okern = time_calls(decode_slots_sorted, args.steps, args.warmup, torch)
+        oms, okern = time_calls(decode_slots_sorted, args.steps, args.warmup, torch, warm_s=0.2)
         okms = okern.get("gdn_decode_step", (0, oms))[1]
         del pool_s
         st_n = dd["s0"].clone()
@@ -593,7 +594,7 @@ def main():
             gdn.gdn_decode_ex(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], st_n, flags=gdn.GDN_FLAG_QK_L2NORM,
                               out=dout)
 
-        qms, qkern = time_calls(decode_norm, args.steps, args.warmup, torch)
+        qms, qkern = time_calls(decode_norm, args.steps, args.warmup, torch, warm_s=0.2)
         qkms = qkern.get("gdn_decode_step", (0, qms))[1]
         result["decode"]["qk_l2norm"] = {"ms_per_step": qms, "kernel_ms_per_launch": qkms,
                                          "GB_per_s": nbytes / (qkms / 1e3) / 1e9,
@@ -635,7 +636,7 @@ def main():
         def decode_multi():
             gdn.gdn_decode_multi(dm["q"], dm["k"], dm["v"], dm["g"], dm["beta"], stm, tk, out=om)
 
-        mms, mkern = time_calls(decode_multi, args.steps, args.warmup, torch)
+        mms, mkern = time_calls(decode_multi, args.steps, args.warmup, torch, warm_s=0.2)
         mkms = mkern.get("gdn_decode_multi", (0, mms))[1]
         mbytes = decode_bytes(n, tokens=tk)
         mgbs = mbytes / (mkms / 1e3) / 1e9
@@ -666,7 +667,7 @@ def main():
             gdn.gdn_conv_prologue(xc, wc, None, None, num_qk_heads=hqk, num_v_heads=hv, silu=True, qk_l2norm=True,
                                   q=qc, k=kc_, v=vc, conv_state_out=hc)
 
-        cms, ckern = time_calls(conv, args.steps, max(2, args.warmup // 4), torch)
+        cms, ckern = time_calls(conv, args.steps, max(2, args.warmup // 4), torch, warm_s=0.2)
         cbytes = T * C * 2 * 2 + C * K * 4 + (K - 1) * C * 2
         ckms = ckern.get("gdn_conv_prologue", (0, cms))[1]
         cgbs = cbytes / (ckms / 1e3) / 1e9
@@ -696,7 +697,7 @@ def main():
                                   qk_l2norm=True, q=qd, k=kd, v=vd, conv_state_out=hd)
             gdn.gdn_decode_step(qd, kd, vd, dd_["g"], dd_["beta"], st, out=od)
 
-        dms_, dkern_ = time_calls(conv_decode, args.steps, max(2, args.warmup // 4), torch)
+        dms_, dkern_ = time_calls(conv_decode, args.steps, max(2, args.warmup // 4), torch, warm_s=0.2)
         result["conv_prologue"]["decode_with_prologue"] = {
             "workload": cd.name, "ms_per_step": dms_, "tokens_per_s": n / (dms_ / 1e3),
             "kernels_ms_per_launch": {k_: v_[1] for k_, v_ in dkern_.items()}}
@@ -710,7 +711,7 @@ def main():
                                 conv_state_out=hist_pair[1], silu=True, qk_l2norm=True, out=od)
             hist_pair.reverse()
 
-        fms_, fkern_ = time_calls(conv_decode_fused, args.steps, max(2, args.warmup // 4), torch)
+        fms_, fkern_ = time_calls(conv_decode_fused, args.steps, max(2, args.warmup // 4), torch, warm_s=0.2)
         fkms = fkern_.get("gdn_decode_conv", (0, fms_))[1]
         C_ = (2 * hqk + hv) * dd
         fbytes = (n * hv * dd * dd * 4 * 2 + n * C_ * 2 + 2 * n * (K - 1) * C_ * 2 + n * hv * 4 * 2 + n * hv * dd * 2

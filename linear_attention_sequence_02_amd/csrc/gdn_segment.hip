@@ -18,7 +18,8 @@
 //   pass A   every segment but a sequence's last: H (segment 0 starts from
 //            the sequence's initial state, so its H is its end state) and,
 //            for segments >= 1, M.
-//   combine  S_in(1) = H_0, S_in(j+1) = S_in(j) M_j + H_j, in fp32.
+//   combine  S_in(1) = H_0, S_in(j+1) = S_in(j) M_j + H_j, fp32 values (products
+//            split into bf16 parts on MFMA, fp32 accumulation).
 //   pass C   every segment from its true entry state: outputs and, for the
 //            last segment, the final state.
 //
@@ -818,17 +819,31 @@ __global__ __launch_bounds__(64 * (4 + kProd)) void segment_kernel(
 }
 
 
-// Combine, fp32: for each (sequence, V head, block of 16 state rows), walk the
+// Combine: for each (sequence, V head, block of 16 state rows), walk the
 // sequence's segments: S_in(1) = H_0, S_in(j+1) = S_in(j) M_j + H_j; S_in(j) is
-// stored for pass C. Each wave computes 32 of the 128 columns with fp32 MFMA
-// 16x16x4 (lane (g, m): A[m][k], B[k][m] with k = 4 kk + g; D[4 g + e][m]);
+// stored for pass C. Each wave computes 32 of the 128 columns with the products
+// split into bf16 parts on MFMA 16x16x32 (fp32 accumulation; S_in, M and H stay
+// fp32 in memory and the split keeps about fp32 accuracy);
 // M_{j+1} and H_{j+1} do not depend on the recurrence and are loaded during
 // step j, so only the 16 rows of S_in pass through LDS between steps. The row
 // blocks of one (sequence, head) are consecutive in units of the head count,
 // which puts them on one XCD (blocks go round-robin to the 8 XCDs) when the
 // head count is a multiple of 8: M_j then comes from HBM once.
-__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+// x = hi + lo in bf16 (hi = x rounded to nearest even, lo = the rest rounded): the products below
+// take hi·hi + hi·lo + lo·hi, which leaves out lo·lo (at most 2^-18 of the product); with the
+// rounding of lo the error stays near 1e-5 of each product, on bf16 MFMA.
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t ph = pack_bf16(x[2 * i], x[2 * i + 1]);
+        const float r0 = x[2 * i] - __uint_as_float(ph << 16);
+        const float r1 = x[2 * i + 1] - __uint_as_float(ph & 0xFFFF0000u);
+        h[i] = ph;
+        l[i] = pack_bf16(r0, r1);
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ cu, float* __restrict__ segws,
@@ -858,15 +873,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
 #pragma unroll
             for (int e = 0; e < 4; ++e) t[ct][e] = X[(size_t)(r0 + 4 * g + e) * D + cb + 16 * ct + m];
     };
-    // B operand of M: row 4 kk + g, column cb + 16 ct + m.
-    auto load_m = [&](const float* M, float (&b)[32][2]) {
+    // B operand of M (16x16x32 bf16 layout): rows 32 kk + 8 g + i, column cb + 16 ct + m.
+    auto load_m = [&](const float* M, float (&b)[4][2][8]) {
 #pragma unroll
-        for (int kk = 0; kk < 32; ++kk)
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) b[kk][ct] = M[(size_t)(4 * kk + g) * D + cb + 16 * ct + m];
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) b[kk][ct][i] = M[(size_t)(32 * kk + 8 * g + i) * D + cb + 16 * ct + m];
     };
     f32x4 acc[2], hn[2];
-    float bm[32][2];
+    float bm[4][2][8];
     load_rows(mat(0, 0), acc);                 // S_in(1) = H_0
     if (nseg > 2) {
         load_m(mat(1, 1), bm);
@@ -887,10 +904,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
         acc[0] = hn[0];
         acc[1] = hn[1];
 #pragma unroll
-        for (int kk = 0; kk < 32; ++kk) {
-            const float a = Srow[m][4 * kk + g];
-            acc[0] = mfma_f32_16x16x4(a, bm[kk][0], acc[0]);
-            acc[1] = mfma_f32_16x16x4(a, bm[kk][1], acc[1]);
+        for (int kk = 0; kk < 4; ++kk) {
+            float a8[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a8[i] = Srow[m][32 * kk + 8 * g + i];
+            bf16x8 ah, al;
+            split_bf16x8(a8, ah, al);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                bf16x8 bh, bl;
+                split_bf16x8(bm[kk][ct], bh, bl);
+                acc[ct] = mfma16(al, bh, acc[ct]);
+                acc[ct] = mfma16(ah, bl, acc[ct]);
+                acc[ct] = mfma16(ah, bh, acc[ct]);
+            }
         }
         if (jj + 1 < nseg - 1) {
             load_m(mat(jj + 1, 1), bm);
