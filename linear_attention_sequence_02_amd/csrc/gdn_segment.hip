@@ -30,7 +30,8 @@
 //   producer waves  (4) meanwhile build chunk c + 1's factors (masked Gram
 //                   blocks, diagonal-block inverses, decay vectors) and stage
 //                   chunk c + 2's K (and Q) tiles from registers into LDS.
-// K/Q tiles are triple-buffered and the factors double-buffered, so one
+// K/Q tiles are triple-buffered (in the output pass with keys and rows
+// reordered, see kq_row) and the factors double-buffered, so one
 // workgroup barrier per chunk separates producers from consumers. Values and
 // outputs go straight between HBM and the chain waves' registers.
 #include "gdn_mfma.h"
@@ -175,6 +176,52 @@ __device__ __forceinline__ u32x4 l2norm_piece(u32x4 x) {
     return x;
 }
 
+// Output-pass K and Q tiles. Within each 32-key block the keys are held in the
+// order 4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3 for g = 0..3 (the key order of
+// the state's MFMA B operand), so that the chain's K S^T and Q S^T operands are
+// single 16-byte reads instead of two 8-byte ones; products that reduce over
+// the keys (the Gram blocks) read both operands in this order and are
+// unchanged. Token row r is stored at row kq_row(r), which transposes 4 x 4
+// within each 16 rows (r = 16 i + 4 a + b -> 16 i + 4 b + a): with the 136-wide
+// rows, the 16-byte reads of 16 consecutive rows and the transposed reads of
+// the state update (4 rows x 4 key blocks per 16 lanes) then fall on distinct
+// banks. The map pass keeps natural key and row order: holding two states, its
+// registers are at the limit, and the single-read form made the compiler spill.
+__device__ __forceinline__ int kq_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Column of natural keys 8 c8 .. 8 c8 + 3 (keys 8 c8 + 4 .. + 7 follow eight columns further).
+__device__ __forceinline__ int kq_col(int c8) { return 32 * (c8 >> 2) + 16 * (c8 & 1) + 4 * ((c8 >> 1) & 1); }
+
+// MFMA operand (lane (g, m) of a 16x16x32 step kk): token row `row`, keys
+// 32 kk + 4 g .. + 3 and 32 kk + 16 + 4 g .. + 3.
+__device__ __forceinline__ bf16x8 kq_row8(const uint16_t* tile, int row, int kk, int g) {
+    return lds_row8(tile, RP, kq_row(row), kk, g);
+}
+
+// A operand of K^T (row = key 16 t + m, reduction = tokens) in accumulator
+// order: slots 0..3 are tokens 32 kk + 4 g + 0..3 and slots 4..7 tokens
+// 32 kk + 16 + 4 g + 0..3. Lane (g, m) addresses token row 32 kk + 4 g + m / 4
+// at natural keys 16 t + 4 (m % 4) .. + 3; the row 16 tokens later is 16 rows
+// further.
+__device__ __forceinline__ bf16x8 kq_kt_tr(const uint16_t* K, int t, int kk, int g, int m) {
+    const uint16_t* p = K + kq_row(32 * kk + 4 * g + (m >> 2)) * RP + 32 * (t >> 1) + 8 * (m & 3) + 4 * (t & 1);
+    const i16x4 lo = lds_read_tr16(p);
+    const i16x4 hi = lds_read_tr16(p + 16 * RP);
+    u32x4 u;
+    u.x = __builtin_bit_cast(u32x2, lo).x;
+    u.y = __builtin_bit_cast(u32x2, lo).y;
+    u.z = __builtin_bit_cast(u32x2, hi).x;
+    u.w = __builtin_bit_cast(u32x2, hi).y;
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// K-type operand of a Gram product in either pass's tile layout.
+template <int MODE>
+__device__ __forceinline__ bf16x8 tile_row8(const uint16_t* tile, int row, int kk, int g) {
+    if constexpr (MODE == kModeOut) return kq_row8(tile, row, kk, g);
+    else return lds_row8(tile, RP, row, kk, g);
+}
+
 // Rows past the end of a partial chunk were read as zero.
 template <int MODE>
 __device__ __forceinline__ void prod_stage_kq(SegSmem<MODE>& sm, int buf, const ProdRegs& pr, int pl, bool qk_norm) {
@@ -182,9 +229,17 @@ __device__ __forceinline__ void prod_stage_kq(SegSmem<MODE>& sm, int buf, const 
     for (int i = 0; i < 4; ++i) {
         const int p = pl + 256 * i;
         const int row = p >> 4, c8 = p & 15;
-        *reinterpret_cast<u32x4*>(&sm.K[buf][row][c8 * 8]) = qk_norm ? l2norm_piece(pr.k[i]) : pr.k[i];
-        if (MODE == kModeOut)
-            *reinterpret_cast<u32x4*>(&sm.Q[buf][row][c8 * 8]) = qk_norm ? l2norm_piece(pr.q[i]) : pr.q[i];
+        const u32x4 kv = qk_norm ? l2norm_piece(pr.k[i]) : pr.k[i];
+        if constexpr (MODE == kModeOut) {
+            const int pr_ = kq_row(row), col = kq_col(c8);
+            const u32x4 qv = qk_norm ? l2norm_piece(pr.q[i]) : pr.q[i];
+            *reinterpret_cast<u32x2*>(&sm.K[buf][pr_][col]) = u32x2{kv[0], kv[1]};
+            *reinterpret_cast<u32x2*>(&sm.K[buf][pr_][col + 8]) = u32x2{kv[2], kv[3]};
+            *reinterpret_cast<u32x2*>(&sm.Q[buf][pr_][col]) = u32x2{qv[0], qv[1]};
+            *reinterpret_cast<u32x2*>(&sm.Q[buf][pr_][col + 8]) = u32x2{qv[2], qv[3]};
+        } else {
+            *reinterpret_cast<u32x4*>(&sm.K[buf][row][c8 * 8]) = kv;
+        }
     }
 }
 
@@ -203,11 +258,12 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 
 // 16 x 16 Gram block: rows 16 mt .. of X times rows 16 nt .. of K, transposed;
 // lane (g, m) gets element [16 mt + 4 g + e][16 nt + m].
+template <int MODE>
 __device__ __forceinline__ f32x4 gram_block(const uint16_t* X, const uint16_t* K, int mt, int nt, int g, int m) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-        acc = mfma16(lds_row8(X, RP, 16 * mt + m, kk, g), lds_row8(K, RP, 16 * nt + m, kk, g), acc);
+        acc = mfma16(tile_row8<MODE>(X, 16 * mt + m, kk, g), tile_row8<MODE>(K, 16 * nt + m, kk, g), acc);
     return acc;
 }
 
@@ -248,7 +304,7 @@ __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFac
         float* Ad = sm.Ad;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const f32x4 acc = gram_block(K, K, b, b, g, m);
+            const f32x4 acc = gram_block<MODE>(K, K, b, b, g, m);
             const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[0][16 * b + 4 * g]);
             const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[0][16 * b + 4 * g]);
             const float gc = sm.pg[0][16 * b + m];
@@ -324,7 +380,7 @@ __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFac
             const int jt = job < NJOBS ? job : NJOBS - 1;
             const int mt = (int)((kRow >> (4 * jt)) & 15), nt = (int)((kCol >> (4 * jt)) & 15);
             const bool isP = jt >= 6;
-            const f32x4 acc = gram_block(isP ? Q : K, K, mt, nt, g, m);
+            const f32x4 acc = gram_block<MODE>(isP ? Q : K, K, mt, nt, g, m);
             const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[pw][16 * mt + 4 * g]);
             const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[pw][16 * mt + 4 * g]);
             const float gc = sm.pg[pw][16 * nt + m];
@@ -423,8 +479,8 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
         bf16x8 ka[2][4], qa[2][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            ka[0][mt] = lds_a_perm(K, RP, 16 * mt + m, 0, g);
-            qa[0][mt] = lds_a_perm(Q, RP, 16 * mt + m, 0, g);
+            ka[0][mt] = kq_row8(K, 16 * mt + m, 0, g);
+            qa[0][mt] = kq_row8(Q, 16 * mt + m, 0, g);
         }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -432,8 +488,8 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
             if (kk < 3) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
-                    ka[cur ^ 1][mt] = lds_a_perm(K, RP, 16 * mt + m, kk + 1, g);
-                    qa[cur ^ 1][mt] = lds_a_perm(Q, RP, 16 * mt + m, kk + 1, g);
+                    ka[cur ^ 1][mt] = kq_row8(K, 16 * mt + m, kk + 1, g);
+                    qa[cur ^ 1][mt] = kq_row8(Q, 16 * mt + m, kk + 1, g);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -542,8 +598,8 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
     const float Glast = F.Gam[kChunk - 1];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const bf16x8 a0 = lds_kt_tr(K, RP, t, 0, g, m);
-        const bf16x8 a1 = lds_kt_tr(K, RP, t, 1, g, m);
+        const bf16x8 a0 = WITH_OUT ? kq_kt_tr(K, t, 0, g, m) : lds_kt_tr(K, RP, t, 0, g, m);
+        const bf16x8 a1 = WITH_OUT ? kq_kt_tr(K, t, 1, g, m) : lds_kt_tr(K, RP, t, 1, g, m);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             f32x4 acc = ST[t][nt] * Glast;
