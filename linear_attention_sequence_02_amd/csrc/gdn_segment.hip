@@ -25,15 +25,16 @@
 //
 // Work split inside a workgroup (one (segment, V head)):
 //   chain waves     each owns 32 value columns of a 128 x 128 fp32 state (pass
-//                   C: one state over 4 waves; pass A: H and M over 8 waves),
+//                   C: one state; pass A: H and M, each wave running both),
 //                   held in MFMA accumulators, and runs chunk c.
 //   producer waves  (4) meanwhile build chunk c + 1's factors (masked Gram
 //                   blocks, diagonal-block inverses, decay vectors) and stage
-//                   chunk c + 2's K (and Q) tiles from registers into LDS.
-// K/Q tiles are triple-buffered (in the output pass with keys and rows
-// reordered, see kq_row) and the factors double-buffered, so one
-// workgroup barrier per chunk separates producers from consumers. Values and
-// outputs go straight between HBM and the chain waves' registers.
+//                   chunk c + 2's K and Q (pass C) or K and V (pass A) tiles
+//                   from registers into LDS.
+// The tiles are triple-buffered (K and Q with keys and rows reordered, see
+// kq_row) and the factors double-buffered, so one workgroup barrier per chunk
+// separates producers from consumers. In pass C values and outputs go straight
+// between HBM and the chain waves' registers.
 #include "gdn_mfma.h"
 
 namespace gdn {
@@ -85,10 +86,23 @@ struct __attribute__((aligned(16))) ChunkFactors {
     float Gam[kChunk], Gs[kChunk], bet[kChunk];   // Gamma, scale * Gamma, beta
 };
 
+// Second tile set: queries (output pass) or values (map pass). Map-pass values
+// are held per 4-row group and value-column pair: V[rg][p][e] is the bf16 pair
+// (columns 2 p, 2 p + 1) of token row 4 rg + e, so that a chain lane reads its
+// four rows of one column pair as one 16-byte word.
+template <int MODE>
+struct QVTiles {
+    uint16_t Q[3][kChunk][RP];
+};
+template <>
+struct QVTiles<kModeHM> {
+    uint32_t V[3][kChunk / 4][D / 2][4];
+};
+
 template <int MODE>
 struct __attribute__((aligned(16))) SegSmem {
-    uint16_t K[3][kChunk][RP];                          // keys, token-major
-    uint16_t Q[(MODE == kModeOut) ? 3 : 1][kChunk][RP]; // queries (output pass)
+    uint16_t K[3][kChunk][RP];                          // keys, token-major (layout: kq_row, kq_col)
+    QVTiles<MODE> qv;
     ChunkFactors F[2];
     float Ad[4 * AB];                                   // producer scratch: the diagonal blocks of A
     float Dec[kChunk];                                  // producer scratch: exp(gamma_last - gamma)
@@ -125,8 +139,9 @@ __device__ __forceinline__ void buf_st_b32(uint32_t x, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b32(x, r, (int)off, 0, 0);
 }
 
-// Producer registers: K (and Q) 16-byte pieces of the chunk two ahead, and g,
-// beta (row = lane) of the chunk one ahead.
+// Producer registers: K and Q (output pass) or V (map pass) pieces of the chunk
+// two ahead, and g, beta (row = lane) of the chunk one ahead. Map pass: q[i][e]
+// holds the value-column pair pl % 64 of row 4 (pl / 64 + 4 i) + e.
 struct ProdRegs {
     u32x4 k[4], q[4];
     float g, b;     // the chunk whose factors are built next
@@ -138,15 +153,28 @@ struct ProdRegs {
 // Piece i of producer lane pl: row 16 i + pl / 16, 16-byte column block pl %
 // 16. Rows past nc read as zero.
 template <int MODE>
-__device__ __forceinline__ void prod_fetch_kq(ProdRegs& pr, const uint16_t* kc, const uint16_t* qc, int nc, int ldk,
-                                              int pl) {
+__device__ __forceinline__ void prod_fetch_kq(ProdRegs& pr, const uint16_t* kc, const uint16_t* qc, const uint16_t* vc,
+                                              int nc, int ldk, int ldv, int pl) {
     const rsrc_t rk = chunk_rsrc(uniform_ptr(kc), (int64_t)nc * ldk * 2);
-    const rsrc_t rq = chunk_rsrc(uniform_ptr(qc), (int64_t)nc * ldk * 2);
+    if constexpr (MODE == kModeOut) {
+        const rsrc_t rq = chunk_rsrc(uniform_ptr(qc), (int64_t)nc * ldk * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t off = (uint32_t)(((pl >> 4) + 16 * i) * ldk + (pl & 15) * 8) * 2u;
-        pr.k[i] = buf_ld_b128(rk, off);
-        if (MODE == kModeOut) pr.q[i] = buf_ld_b128(rq, off);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off = (uint32_t)(((pl >> 4) + 16 * i) * ldk + (pl & 15) * 8) * 2u;
+            pr.k[i] = buf_ld_b128(rk, off);
+            pr.q[i] = buf_ld_b128(rq, off);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            pr.k[i] = buf_ld_b128(rk, (uint32_t)(((pl >> 4) + 16 * i) * ldk + (pl & 15) * 8) * 2u);
+        // one wave's load: 64 consecutive column pairs of one row (256 bytes)
+        const rsrc_t rv = chunk_rsrc(uniform_ptr(vc), (int64_t)nc * ldv * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                pr.q[i][e] = buf_ld_b32(rv, (uint32_t)((4 * ((pl >> 6) + 4 * i) + e) * ldv + 2 * (pl & 63)) * 2u);
     }
 }
 
@@ -176,7 +204,7 @@ __device__ __forceinline__ u32x4 l2norm_piece(u32x4 x) {
     return x;
 }
 
-// Output-pass K and Q tiles. Within each 32-key block the keys are held in the
+// K and Q tiles. Within each 32-key block the keys are held in the
 // order 4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3 for g = 0..3 (the key order of
 // the state's MFMA B operand), so that the chain's K S^T and Q S^T operands are
 // single 16-byte reads instead of two 8-byte ones; products that reduce over
@@ -185,8 +213,7 @@ __device__ __forceinline__ u32x4 l2norm_piece(u32x4 x) {
 // within each 16 rows (r = 16 i + 4 a + b -> 16 i + 4 b + a): with the 136-wide
 // rows, the 16-byte reads of 16 consecutive rows and the transposed reads of
 // the state update (4 rows x 4 key blocks per 16 lanes) then fall on distinct
-// banks. The map pass keeps natural key and row order: holding two states, its
-// registers are at the limit, and the single-read form made the compiler spill.
+// banks.
 __device__ __forceinline__ int kq_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // Column of natural keys 8 c8 .. 8 c8 + 3 (keys 8 c8 + 4 .. + 7 follow eight columns further).
@@ -202,9 +229,10 @@ __device__ __forceinline__ bf16x8 kq_row8(const uint16_t* tile, int row, int kk,
 // order: slots 0..3 are tokens 32 kk + 4 g + 0..3 and slots 4..7 tokens
 // 32 kk + 16 + 4 g + 0..3. Lane (g, m) addresses token row 32 kk + 4 g + m / 4
 // at natural keys 16 t + 4 (m % 4) .. + 3; the row 16 tokens later is 16 rows
-// further.
-__device__ __forceinline__ bf16x8 kq_kt_tr(const uint16_t* K, int t, int kk, int g, int m) {
-    const uint16_t* p = K + kq_row(32 * kk + 4 * g + (m >> 2)) * RP + 32 * (t >> 1) + 8 * (m & 3) + 4 * (t & 1);
+// further. lane_off is this lane's part of the address, kq_kt_tr_lane(g, m).
+__device__ __forceinline__ int kq_kt_tr_lane(int g, int m) { return kq_row(4 * g + (m >> 2)) * RP + 8 * (m & 3); }
+__device__ __forceinline__ bf16x8 kq_kt_tr(const uint16_t* K, int t, int kk, int lane_off) {
+    const uint16_t* p = K + 32 * kk * RP + lane_off + 32 * (t >> 1) + 4 * (t & 1);
     const i16x4 lo = lds_read_tr16(p);
     const i16x4 hi = lds_read_tr16(p + 16 * RP);
     u32x4 u;
@@ -215,13 +243,6 @@ __device__ __forceinline__ bf16x8 kq_kt_tr(const uint16_t* K, int t, int kk, int
     return __builtin_bit_cast(bf16x8, u);
 }
 
-// K-type operand of a Gram product in either pass's tile layout.
-template <int MODE>
-__device__ __forceinline__ bf16x8 tile_row8(const uint16_t* tile, int row, int kk, int g) {
-    if constexpr (MODE == kModeOut) return kq_row8(tile, row, kk, g);
-    else return lds_row8(tile, RP, row, kk, g);
-}
-
 // Rows past the end of a partial chunk were read as zero.
 template <int MODE>
 __device__ __forceinline__ void prod_stage_kq(SegSmem<MODE>& sm, int buf, const ProdRegs& pr, int pl, bool qk_norm) {
@@ -230,15 +251,15 @@ __device__ __forceinline__ void prod_stage_kq(SegSmem<MODE>& sm, int buf, const 
         const int p = pl + 256 * i;
         const int row = p >> 4, c8 = p & 15;
         const u32x4 kv = qk_norm ? l2norm_piece(pr.k[i]) : pr.k[i];
+        const int pr_ = kq_row(row), col = kq_col(c8);
+        *reinterpret_cast<u32x2*>(&sm.K[buf][pr_][col]) = u32x2{kv[0], kv[1]};
+        *reinterpret_cast<u32x2*>(&sm.K[buf][pr_][col + 8]) = u32x2{kv[2], kv[3]};
         if constexpr (MODE == kModeOut) {
-            const int pr_ = kq_row(row), col = kq_col(c8);
             const u32x4 qv = qk_norm ? l2norm_piece(pr.q[i]) : pr.q[i];
-            *reinterpret_cast<u32x2*>(&sm.K[buf][pr_][col]) = u32x2{kv[0], kv[1]};
-            *reinterpret_cast<u32x2*>(&sm.K[buf][pr_][col + 8]) = u32x2{kv[2], kv[3]};
-            *reinterpret_cast<u32x2*>(&sm.Q[buf][pr_][col]) = u32x2{qv[0], qv[1]};
-            *reinterpret_cast<u32x2*>(&sm.Q[buf][pr_][col + 8]) = u32x2{qv[2], qv[3]};
+            *reinterpret_cast<u32x2*>(&sm.qv.Q[buf][pr_][col]) = u32x2{qv[0], qv[1]};
+            *reinterpret_cast<u32x2*>(&sm.qv.Q[buf][pr_][col + 8]) = u32x2{qv[2], qv[3]};
         } else {
-            *reinterpret_cast<u32x4*>(&sm.K[buf][row][c8 * 8]) = kv;
+            *reinterpret_cast<u32x4*>(&sm.qv.V[buf][(pl >> 6) + 4 * i][pl & 63][0]) = pr.q[i];
         }
     }
 }
@@ -258,12 +279,11 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 
 // 16 x 16 Gram block: rows 16 mt .. of X times rows 16 nt .. of K, transposed;
 // lane (g, m) gets element [16 mt + 4 g + e][16 nt + m].
-template <int MODE>
 __device__ __forceinline__ f32x4 gram_block(const uint16_t* X, const uint16_t* K, int mt, int nt, int g, int m) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-        acc = mfma16(tile_row8<MODE>(X, 16 * mt + m, kk, g), tile_row8<MODE>(K, 16 * nt + m, kk, g), acc);
+        acc = mfma16(kq_row8(X, 16 * mt + m, kk, g), kq_row8(K, 16 * nt + m, kk, g), acc);
     return acc;
 }
 
@@ -284,7 +304,8 @@ template <int MODE>
 __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFactors& F, const ProdRegs& pr, int nc,
                                              float scale, int pw, int lane) {
     const uint16_t* K = &sm.K[kb][0][0];
-    const uint16_t* Q = &sm.Q[(MODE == kModeOut) ? kb : 0][0][0];
+    const uint16_t* Q = K;
+    if constexpr (MODE == kModeOut) Q = &sm.qv.Q[kb][0][0];
     const int g = lane >> 4, m = lane & 15;
 
     // gamma = in-chunk inclusive prefix sum of g; rows past nc add 0 and have beta 0.
@@ -304,7 +325,7 @@ __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFac
         float* Ad = sm.Ad;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const f32x4 acc = gram_block<MODE>(K, K, b, b, g, m);
+            const f32x4 acc = gram_block(K, K, b, b, g, m);
             const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[0][16 * b + 4 * g]);
             const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[0][16 * b + 4 * g]);
             const float gc = sm.pg[0][16 * b + m];
@@ -380,7 +401,7 @@ __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFac
             const int jt = job < NJOBS ? job : NJOBS - 1;
             const int mt = (int)((kRow >> (4 * jt)) & 15), nt = (int)((kCol >> (4 * jt)) & 15);
             const bool isP = jt >= 6;
-            const f32x4 acc = gram_block<MODE>(isP ? Q : K, K, mt, nt, g, m);
+            const f32x4 acc = gram_block(isP ? Q : K, K, mt, nt, g, m);
             const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[pw][16 * mt + 4 * g]);
             const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[pw][16 * mt + 4 * g]);
             const float gc = sm.pg[pw][16 * nt + m];
@@ -399,7 +420,7 @@ __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFac
         auto job = [&](int mt, int nt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mfma16(lds_row8(K, RP, 16 * mt + m, kk, g), kc[kk], acc);
+            for (int kk = 0; kk < 4; ++kk) acc = mfma16(kq_row8(K, 16 * mt + m, kk, g), kc[kk], acc);
             const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[pw][16 * mt + 4 * g]);
             const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[pw][16 * mt + 4 * g]);
             const float gc = sm.pg[pw][16 * nt + m];
@@ -410,7 +431,7 @@ __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFac
         };
         const int nt = pw - 1;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kc[kk] = lds_row8(K, RP, 16 * nt + m, kk, g);
+        for (int kk = 0; kk < 4; ++kk) kc[kk] = kq_row8(K, 16 * nt + m, kk, g);
         if (pw == 1) {
             job(1, 0);
             job(2, 0);
@@ -458,11 +479,15 @@ __device__ __forceinline__ void chain_fetch_v(uint32_t (&vr)[16], const uint16_t
 // columns cb + 2 m (tile nt = 0) and cb + 2 m + 1 (nt = 1). ST[t][nt] element e
 // is S[column][key 16 t + 4 g + e]. vin holds this chunk's values; the next
 // chunk's (from vnext) are requested into vout.
+// Values: the output pass holds them in registers (vin; the next chunk's go to
+// vout); the map pass reads this chunk's from LDS (vl: this lane's column pair
+// of row group 0).
 template <bool WITH_V, bool WITH_OUT>
 __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q, const ChunkFactors& F,
                                            f32x4 (&ST)[8][2], const uint32_t (&vin)[16], uint32_t (&vout)[16],
                                            const uint16_t* vnext, int ncn,
-                                           uint16_t* orow0, int ldv, int nc, float scale, int g, int m) {
+                                           uint16_t* orow0, int ldv, int nc, float scale, int g, int m,
+                                           const uint32_t* vl) {
     // Z = K S^T and, for the output, Y = Q S^T: one pass over the S^T operands.
     f32x4 X[4][2], Y[4][2];
 #pragma unroll
@@ -512,13 +537,18 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
             const bf16x8 sb1 = pack_acc_pair(ST[2 * kk][1], ST[2 * kk + 1][1]);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 a = lds_a_perm(K, RP, 16 * mt + m, kk, g);
+                const bf16x8 a = kq_row8(K, 16 * mt + m, kk, g);
                 X[mt][0] = mfma16(a, sb0, X[mt][0]);
                 X[mt][1] = mfma16(a, sb1, X[mt][1]);
             }
         }
     }
     // X = beta (V - Gamma Z); then the next chunk's values are requested.
+    u32x4 vw[4];
+    if constexpr (WITH_V && !WITH_OUT) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) vw[mt] = *reinterpret_cast<const u32x4*>(vl + (4 * mt + g) * (D / 2) * 4);
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const f32x4 Gr = *reinterpret_cast<const f32x4*>(&F.Gam[16 * mt + 4 * g]);
@@ -527,8 +557,9 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
         for (int e = 0; e < 4; ++e) {
             float v0 = 0.f, v1 = 0.f;
             if (WITH_V) {
-                v0 = __uint_as_float(vin[4 * mt + e] << 16);
-                v1 = __uint_as_float(vin[4 * mt + e] & 0xFFFF0000u);
+                const uint32_t x = WITH_OUT ? vin[4 * mt + e] : vw[mt][e];
+                v0 = __uint_as_float(x << 16);
+                v1 = __uint_as_float(x & 0xFFFF0000u);
             }
             X[mt][0][e] = Br[e] * (v0 - Gr[e] * X[mt][0][e]);
             X[mt][1][e] = Br[e] * (v1 - Gr[e] * X[mt][1][e]);
@@ -538,7 +569,7 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
     // consumed: global loads complete in order, so a load hoisted above the
     // uses of the previous ones would make those uses wait for it.
     __builtin_amdgcn_sched_barrier(0);
-    if (WITH_V) chain_fetch_v(vout, vnext, ncn, ldv, g, m);
+    if (WITH_V && WITH_OUT) chain_fetch_v(vout, vnext, ncn, ldv, g, m);
     // U by 16-row blocks: U_b = Td_b (X_b - sum A_bb' U_b'), and the state
     // update's exp(gamma_last - gamma) U_b = Tw_b (same right-hand side),
     // packed as soon as a pair of blocks is done.
@@ -596,10 +627,15 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
     }
     // S^T = Gamma_last S^T + K^T (exp(gamma_last - gamma) U)
     const float Glast = F.Gam[kChunk - 1];
+    // Map pass: recomputed every step (the empty asm hides it from loop-invariant
+    // code motion): hoisted out of the chunk loop, the sixteen addresses derived
+    // from it occupied registers for the whole loop and made the compiler spill.
+    int tro = kq_kt_tr_lane(g, m);
+    if constexpr (!WITH_OUT) asm volatile("" : "+v"(tro));
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const bf16x8 a0 = WITH_OUT ? kq_kt_tr(K, t, 0, g, m) : lds_kt_tr(K, RP, t, 0, g, m);
-        const bf16x8 a1 = WITH_OUT ? kq_kt_tr(K, t, 1, g, m) : lds_kt_tr(K, RP, t, 1, g, m);
+        const bf16x8 a0 = kq_kt_tr(K, t, 0, tro);
+        const bf16x8 a1 = kq_kt_tr(K, t, 1, tro);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             f32x4 acc = ST[t][nt] * Glast;
@@ -615,13 +651,15 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
 template <int MODE>
 __device__ __forceinline__ void chain_loop(SegSmem<MODE>& sm, f32x4 (&ST)[8][2], f32x4 (&SM)[8][2], bool with_m,
                                            const uint16_t* vcol, uint16_t* ocol, int64_t bos, int64_t eos,
-                                           int64_t c_begin, int64_t nchunks, int ldv, float scale, int lg, int lm) {
+                                           int64_t c_begin, int64_t nchunks, int ldv, float scale, int lg, int lm,
+                                           int cb) {
     auto chunk_nc = [&](int64_t c) {
         const int64_t rem = eos - (bos + c * kChunk);
         return (int)(rem < kChunk ? rem : kChunk);
     };
     uint32_t va[16];
-    if (nchunks > 0) chain_fetch_v(va, vcol + (bos + c_begin * kChunk) * ldv, chunk_nc(c_begin), ldv, lg, lm);
+    if constexpr (MODE == kModeOut)
+        if (nchunks > 0) chain_fetch_v(va, vcol + (bos + c_begin * kChunk) * ldv, chunk_nc(c_begin), ldv, lg, lm);
     // The entry state and the first values have arrived before the chunk loop
     // starts; otherwise the loop header's wait for the values would also cover
     // every later global access (the previous chunk's output stores included).
@@ -635,32 +673,24 @@ __device__ __forceinline__ void chain_loop(SegSmem<MODE>& sm, f32x4 (&ST)[8][2],
             const int64_t cn = (i + 1 < nchunks) ? c + 1 : c;
             const int64_t t0 = bos + c * kChunk;
             const uint16_t* vnext = vcol + (bos + cn * kChunk) * ldv;
-            chain_step<true, true>(&sm.K[kb][0][0], &sm.Q[kb][0][0], sm.F[i & 1], ST, va, va, vnext, chunk_nc(cn),
-                                   ocol + t0 * ldv, ldv, chunk_nc(c), scale, lg, lm);
+            chain_step<true, true>(&sm.K[kb][0][0], &sm.qv.Q[kb][0][0], sm.F[i & 1], ST, va, va, vnext,
+                                   chunk_nc(cn), ocol + t0 * ldv, ldv, chunk_nc(c), scale, lg, lm, nullptr);
             lds_barrier();
         }
     } else {
-        // Map pass: two value register sets, the loop unrolled by two, so that
-        // the values requested during chunk i land in the set chunk i + 1
-        // reads (with one set, register copies at the loop's back edge waited
-        // for them before each chunk's barrier).
-        uint32_t vb[16];
-        auto chunk = [&](int64_t i, const uint32_t (&vin)[16], uint32_t (&vout)[16]) {
+        // Map pass: the H chain (values from LDS) and, when `with_m`, the M
+        // chain (no values) for the same columns.
+        for (int64_t i = 0; i < nchunks; ++i) {
             const int64_t c = c_begin + i;
             const int kb = (int)(i % 3);
-            const int64_t cn = (i + 1 < nchunks) ? c + 1 : c;
-            const uint16_t* vnext = vcol + (bos + cn * kChunk) * ldv;
-            chain_step<true, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], ST, vin, vout, vnext, chunk_nc(cn),
-                                    nullptr, ldv, chunk_nc(c), scale, lg, lm);
+            const uint32_t* vl = &sm.qv.V[kb][0][cb / 2 + lm][0];
+            chain_step<true, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], ST, va, va, nullptr, 0, nullptr, ldv,
+                                    chunk_nc(c), scale, lg, lm, vl);
             __builtin_amdgcn_sched_barrier(0);   // keep the H and M steps' temporaries apart
             if (with_m)
-                chain_step<false, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], SM, vout, vout, nullptr, 0, nullptr,
-                                         ldv, chunk_nc(c), scale, lg, lm);
+                chain_step<false, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], SM, va, va, nullptr, 0, nullptr,
+                                         ldv, chunk_nc(c), scale, lg, lm, nullptr);
             lds_barrier();
-        };
-        for (int64_t i = 0; i < nchunks; i += 2) {
-            chunk(i, va, vb);
-            if (i + 1 < nchunks) chunk(i + 1, vb, va);
         }
     }
 }
@@ -726,7 +756,8 @@ __device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A
     ProdRegs pr;
     auto fetch_kq = [&](int64_t c) {
         const int64_t t0 = chunk_t0(c);
-        prod_fetch_kq<MODE>(pr, k + t0 * ldk + hq * D, q + t0 * ldk + hq * D, chunk_nc(c), ldk, pl);
+        prod_fetch_kq<MODE>(pr, k + t0 * ldk + hq * D, q + t0 * ldk + hq * D, v + t0 * ldv + h * D, chunk_nc(c), ldk,
+                            ldv, pl);
     };
     auto fetch_gb = [&](int64_t c) {
         const int64_t t0 = chunk_t0(c);
@@ -798,7 +829,7 @@ __device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A
             }
     }
     chain_loop<MODE>(sm, ST, SM, MODE == kModeHM, v + h * D + cb, A.out + h * D + cb, sr.bos, sr.eos, c_begin,
-                     nchunks, ldv, scale, lg, lm);
+                     nchunks, ldv, scale, lg, lm, cb);
 
     if (MODE == kModeOut) {
         // The last segment's end state is the sequence's final state; segment
@@ -840,6 +871,7 @@ __global__ __launch_bounds__(64 * (4 + kProd)) void segment_kernel(
     int64_t total_tokens, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads, int32_t L, int64_t num_segs,
     float scale, int32_t phase, const int32_t* state_indices, const int32_t* has_initial, int32_t num_slots,
     int32_t qk_norm) {
+    static_assert(sizeof(SegSmem<kModeHM>) <= sizeof(SegSmem<kModeOut>), "the map pass reuses the output pass's LDS");
     __shared__ SegSmem<kModeOut> sm;
 
     // XCD-aware placement: workgroups are dealt round-robin to the 8 XCDs
