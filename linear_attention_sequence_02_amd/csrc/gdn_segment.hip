@@ -488,6 +488,12 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
                                            const uint16_t* vnext, int ncn,
                                            uint16_t* orow0, int ldv, int nc, float scale, int g, int m,
                                            const uint32_t* vl) {
+    // Map pass: this chunk's values from LDS, requested before the products.
+    u32x4 vw[4];
+    if constexpr (WITH_V && !WITH_OUT) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) vw[mt] = *reinterpret_cast<const u32x4*>(vl + (4 * mt + g) * (D / 2) * 4);
+    }
     // Z = K S^T and, for the output, Y = Q S^T: one pass over the S^T operands.
     f32x4 X[4][2], Y[4][2];
 #pragma unroll
@@ -530,25 +536,29 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
-        // Map pass (two states held): no room for a second operand set.
+        // Map pass: the same pipelining over the key steps, K only.
+        bf16x8 ka[2][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) ka[0][mt] = kq_row8(K, 16 * mt + m, 0, g);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+            const int cur = kk & 1;
+            if (kk < 3) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) ka[cur ^ 1][mt] = kq_row8(K, 16 * mt + m, kk + 1, g);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             const bf16x8 sb0 = pack_acc_pair(ST[2 * kk][0], ST[2 * kk + 1][0]);
             const bf16x8 sb1 = pack_acc_pair(ST[2 * kk][1], ST[2 * kk + 1][1]);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 a = kq_row8(K, 16 * mt + m, kk, g);
-                X[mt][0] = mfma16(a, sb0, X[mt][0]);
-                X[mt][1] = mfma16(a, sb1, X[mt][1]);
+                X[mt][0] = mfma16(ka[cur][mt], sb0, X[mt][0]);
+                X[mt][1] = mfma16(ka[cur][mt], sb1, X[mt][1]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     // X = beta (V - Gamma Z); then the next chunk's values are requested.
-    u32x4 vw[4];
-    if constexpr (WITH_V && !WITH_OUT) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) vw[mt] = *reinterpret_cast<const u32x4*>(vl + (4 * mt + g) * (D / 2) * 4);
-    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const f32x4 Gr = *reinterpret_cast<const f32x4*>(&F.Gam[16 * mt + 4 * g]);
