@@ -756,7 +756,7 @@ def main():
             gdn.gdn_backward(db["q"], db["k"], db["v"], db["g"], db["beta"], gout, None, None, workspace=wsb)
 
         bsteps = max(2, args.steps // 4)
-        bms, bkern = time_calls(backward, bsteps, 2, torch)
+        bms, bkern = time_calls(backward, bsteps, 2, torch, warm_s=0.3)
         # four stages per call: chunk factors, the two scans, the per-chunk gradients, the fixed-order sums
         bparts = {k: bkern[k][1] for k in ("gdn_backward_prep", "gdn_backward_scan", "gdn_backward_grad",
                                             "gdn_backward_sums") if k in bkern}
