@@ -939,6 +939,24 @@ __global__ void backward_qk_sum_kernel(const float* __restrict__ part, float* __
     dst[e] = s;
 }
 
+// The same sums over 16-byte words, dq (blockIdx.y = 0) and dk (1) in one launch:
+// output word e4 is word e4 % (d / 4) of row e4 / (d / 4) (d / 4 = 1 << lg), and
+// the group's parts of a row are consecutive rows of `part`. The parts are added
+// in the same order as above, so the sums are the same.
+__global__ void backward_qk_sum4_kernel(const float* __restrict__ part_q, const float* __restrict__ part_k,
+                                        float* __restrict__ dq, float* __restrict__ dk, int64_t n4, int32_t group,
+                                        int32_t lg) {
+    const int64_t e4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e4 >= n4) return;
+    const f32x4* part = reinterpret_cast<const f32x4*>(blockIdx.y ? part_k : part_q);
+    f32x4* dst = reinterpret_cast<f32x4*>(blockIdx.y ? dk : dq);
+    const int64_t d4 = (int64_t)1 << lg;
+    const f32x4* p = part + (e4 >> lg) * group * d4 + (e4 & (d4 - 1));
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < group; ++x) s += p[x * d4];
+    dst[e4] = s;
+}
+
 size_t backward_workspace_bytes(int64_t total_tokens, int32_t num_seqs, int32_t num_v_heads, int32_t d) {
     const int64_t slots = total_tokens / kC + num_seqs;
     const size_t ck = (size_t)slots * num_v_heads * d * d * sizeof(float);    // one checkpoint array
@@ -983,10 +1001,20 @@ static hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t stream) {
     const int64_t nqk = a.total_tokens * a.num_qk_heads * D;
     const int group = a.num_v_heads / a.num_qk_heads;
     prof::begin(stream, "gdn_backward_sums");
-    hipLaunchKernelGGL(backward_qk_sum_kernel, dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0, stream, dq_h, a.dq,
-                       a.total_tokens, a.num_qk_heads, group, D);
-    hipLaunchKernelGGL(backward_qk_sum_kernel, dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0, stream, dk_h, a.dk,
-                       a.total_tokens, a.num_qk_heads, group, D);
+    const bool aligned = ((reinterpret_cast<uintptr_t>(dq_h) | reinterpret_cast<uintptr_t>(dk_h) |
+                           reinterpret_cast<uintptr_t>(a.dq) | reinterpret_cast<uintptr_t>(a.dk)) & 15) == 0;
+    if (aligned) {
+        constexpr int lg = D == 16 ? 2 : D == 32 ? 3 : D == 64 ? 4 : 5;
+        static_assert((4 << lg) == D, "d / 4 is a power of two");
+        const int64_t n4 = nqk / 4;
+        hipLaunchKernelGGL(backward_qk_sum4_kernel, dim3((unsigned)((n4 + 255) / 256), 2), dim3(256), 0, stream, dq_h,
+                           dk_h, a.dq, a.dk, n4, group, lg);
+    } else {
+        hipLaunchKernelGGL(backward_qk_sum_kernel, dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0, stream, dq_h,
+                           a.dq, a.total_tokens, a.num_qk_heads, group, D);
+        hipLaunchKernelGGL(backward_qk_sum_kernel, dim3((unsigned)((nqk + 255) / 256)), dim3(256), 0, stream, dk_h,
+                           a.dk, a.total_tokens, a.num_qk_heads, group, D);
+    }
     prof::end(stream);
     return hipGetLastError();
 }
