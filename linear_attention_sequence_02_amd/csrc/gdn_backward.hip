@@ -192,12 +192,20 @@ __global__ __launch_bounds__(64) void backward_prep_kernel(BwdIn in, ChunkFac* _
     int64_t t0;
     if (!slot_chunk(in, sl, n, t0, cnt)) return;
     const int ln = threadIdx.x, g4 = ln / 16, m = ln % 16;
-    for (int e = ln; e < kC * D; e += 64) {
-        const int t = e / D, c = e % D;
+    // K and Q rows in pieces of D / 16 elements (the scan reads its rows in the same pieces).
+    constexpr int NE = D / 16;
+    for (int e = ln; e < kC * 16; e += 64) {
+        const int t = e / 16, c = NE * (e % 16);
         const int64_t idx = ((t0 + min(t, cnt - 1)) * in.num_qk_heads + hq) * D + c;
         const float keep = t < cnt ? 1.f : 0.f;
-        Kf[t][c] = keep * ld_in<BF16>(in.k, idx);
-        Qf[t][c] = keep * ld_in<BF16>(in.q, idx);
+        float kv[NE], qv[NE];
+        ld_vec<BF16, NE>(in.k, idx, kv);
+        ld_vec<BF16, NE>(in.q, idx, qv);
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            Kf[t][c + i] = keep * kv[i];
+            Qf[t][c + i] = keep * qv[i];
+        }
     }
     if (ln < kC) {
         const int64_t gi = (t0 + min(ln, cnt - 1)) * hv + h;
