@@ -298,8 +298,9 @@ __device__ __forceinline__ void store_block_bf16(uint16_t (*blk)[TP], const f32x
 
 // Factors of one chunk (its K/Q tiles in buffer kb) into F. Producer wave 0
 // builds the four diagonal blocks of A and inverts them (lane group g: block
-// g, lane m: column m); waves 1..3 take the off-diagonal A blocks (jobs 0..5)
-// and the P blocks (jobs 6..15) in turn.
+// g, lane m: column m) and, in the output pass, the last diagonal P block (job
+// 15); waves 1..3 take the off-diagonal A blocks (jobs 0..5) and the other P
+// blocks (jobs 6..14) in turn.
 template <int MODE>
 __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFactors& F, const ProdRegs& pr, int nc,
                                              float scale, int pw, int lane) {
@@ -322,16 +323,52 @@ __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFac
         F.bet[lane] = bt;
         sm.Dec[lane] = fast_exp(glast - x);
         // Diagonal blocks of A, fp32, strictly lower: block b = rows/cols 16 b ..
+        // The four blocks are independent and each uses one operand on both sides:
+        // all operand reads first, then the four MFMA chains interleaved.
+        // Output pass: wave 0 also builds the last diagonal P block (Q K^T of rows
+        // 48..63, whose K operand it already holds), so that waves 1..3 share the
+        // other fifteen jobs evenly.
         float* Ad = sm.Ad;
+        bf16x8 kd[4][4], q3[4];
+        f32x4 grd[4], brd[4];
+        float gcd[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const f32x4 acc = gram_block(K, K, b, b, g, m);
-            const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.pg[0][16 * b + 4 * g]);
-            const f32x4 br = *reinterpret_cast<const f32x4*>(&sm.pb[0][16 * b + 4 * g]);
-            const float gc = sm.pg[0][16 * b + m];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) kd[b][kk] = kq_row8(K, 16 * b + m, kk, g);
+            grd[b] = *reinterpret_cast<const f32x4*>(&sm.pg[0][16 * b + 4 * g]);
+            brd[b] = *reinterpret_cast<const f32x4*>(&sm.pb[0][16 * b + 4 * g]);
+            gcd[b] = sm.pg[0][16 * b + m];
+        }
+        if constexpr (MODE == kModeOut) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) q3[kk] = kq_row8(Q, 48 + m, kk, g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 accd[4], accp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) accd[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) accd[b] = mfma16(kd[b][kk], kd[b][kk], accd[b]);
+            if constexpr (MODE == kModeOut) accp = mfma16(q3[kk], kd[3][kk], accp);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MODE == kModeOut) {
+            f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float a = br[e] * fast_exp(gr[e] - gc) * acc[e];
+                const float x = scale * fast_exp(grd[3][e] - gcd[3]) * accp[e];
+                v[e] = (m <= 4 * g + e) ? x : 0.f;
+            }
+            store_block_bf16(F.Ob[15], v, g, m);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = brd[b][e] * fast_exp(grd[b][e] - gcd[b]) * accd[b][e];
                 Ad[b * AB + (4 * g + e) * AP + m] = (m < 4 * g + e) ? a : 0.f;
             }
         }
@@ -389,12 +426,11 @@ __device__ __forceinline__ void prod_factors(SegSmem<MODE>& sm, int kb, ChunkFac
 
     if constexpr (MODE == kModeOut) {
         // Output pass: off-diagonal A blocks (stored negated) and P blocks
-        // (scaled). Waves 1..3 take jobs pw - 1, pw + 2, ... with no branches:
-        // 16 jobs in six rounds, the two rounds past the end write the unused
-        // block 16.
+        // (scaled). Waves 1..3 take jobs pw - 1, pw + 2, ...: fifteen jobs in
+        // five rounds each (block 16 of the factor set stays unused).
         constexpr uint64_t kRow = 0x3333222110333221ull, kCol = 0x3210210100210100ull;
-        constexpr int NJOBS = 16;
-        constexpr int ROUNDS = (NJOBS + 2) / 3;
+        constexpr int NJOBS = 15;   // job 15 (P block (3, 3)) is built by wave 0
+        constexpr int ROUNDS = NJOBS / 3;
 #pragma unroll
         for (int jj = 0; jj < ROUNDS; ++jj) {
             const int job = (pw - 1) + 3 * jj;
