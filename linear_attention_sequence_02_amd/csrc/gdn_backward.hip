@@ -279,7 +279,9 @@ struct ScanShape {
 
 template <int D>
 struct ScanSmem {
-    static constexpr int KP = D + 1, SP = kC + 1;   // odd pitches spread a column over the banks
+    // K, Q rows 16-byte aligned (the commit and the K X^T operands move 16 bytes per
+    // access); the odd pitch of the 16 x 16 matrices spreads a column over the banks.
+    static constexpr int KP = D + 4, SP = kC + 1;
     float Kc[3][kC][KP], Qc[3][kC][KP];
     float Xc[3][kC][SP], Tc[3][kC][SP], Pc[3][kC][SP], Gc[3][kC], Hc[3][kC], bc[3][kC];   // Hc: Gp
     float part[2][4][kC][SP], Uw[4][kC][SP];
