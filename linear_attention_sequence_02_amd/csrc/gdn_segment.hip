@@ -732,7 +732,6 @@ __device__ __forceinline__ void chain_loop(SegSmem<MODE>& sm, f32x4 (&ST)[8][2],
             const uint32_t* vl = &sm.qv.V[kb][0][cb / 2 + lm][0];
             chain_step<true, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], ST, va, va, nullptr, 0, nullptr, ldv,
                                     chunk_nc(c), scale, lg, lm, vl);
-            __builtin_amdgcn_sched_barrier(0);   // keep the H and M steps' temporaries apart
             if (with_m)
                 chain_step<false, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], SM, va, va, nullptr, 0, nullptr,
                                          ldv, chunk_nc(c), scale, lg, lm, nullptr);
