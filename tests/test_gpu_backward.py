@@ -111,3 +111,38 @@ def test_backward_no_tokens():
     assert torch.equal(res["d_initial_state"], d_fin)
     for name in ("dq", "dk", "dv", "dg", "dbeta"):
         assert res[name].shape[0] == 0
+
+
+def test_backward_unaligned_dq_dk():
+    """dq and dk at addresses that are not 16-byte aligned take the one-element-per-thread sums;
+    they add the V heads' parts in the same order as the 16-byte path, so the results are the same
+    bits as with aligned outputs (the layer's 16 QK / 32 V heads, d = 128, a ragged length)."""
+    x = I.draw(lengths=[150], hqk=16, hv=32, dk=128, dtype="bf16", seed=451, s0_std=0.1,
+               scale=128 ** -0.5, name="backward_unaligned")
+    rng = np.random.default_rng(452)
+    dev = to_device(x)
+    d_out = torch.from_numpy(I.f32_to_bf16_bits(rng.standard_normal(x.v.shape).astype(np.float32))).view(
+        torch.bfloat16).cuda()
+    log(f"[gpu] gdn_backward {x.name} T={x.T}, aligned reference")
+    ref = gdn.gdn_backward(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], d_out, dev["s0"], dev["cu"],
+                           scale=x.scale)
+    T, hqk, hv, d = x.T, x.hqk, x.hv, x.dk
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dq_buf = torch.full((T * hqk * d + 1,), float("nan"), **f32)
+    dk_buf = torch.full((T * hqk * d + 1,), float("nan"), **f32)
+    dv, dg, dbeta = torch.empty((T, hv, d), **f32), torch.empty((T, hv), **f32), torch.empty((T, hv), **f32)
+    ds0 = torch.empty((1, hv, d, d), **f32)
+    need = gdn.gdn_backward_workspace_size(T, 1, hqk, hv, d, d, gdn.GDN_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    p = lambda t: t.data_ptr()
+    log(f"[gpu] gdn_backward {x.name}: dq, dk 4 bytes past 16-byte alignment")
+    st = gdn._load().gdn_backward(p(dev["q"]), p(dev["k"]), p(dev["v"]), p(dev["g"]), p(dev["beta"]), p(dev["s0"]),
+                                  p(dev["cu"]), 1, T, hqk, hv, d, d, float(x.scale), gdn.GDN_BF16, p(d_out), None,
+                                  p(dq_buf) + 4, p(dk_buf) + 4, p(dv), p(dg), p(dbeta), p(ds0), p(ws), need,
+                                  torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == gdn.GDN_OK
+    assert p(dq_buf) % 16 == 0   # so that + 4 bytes is not 16-byte aligned
+    assert torch.equal(dq_buf[1:].view(T, hqk, d), ref["dq"])
+    assert torch.equal(dk_buf[1:].view(T, hqk, d), ref["dk"])
+    assert torch.equal(dv, ref["dv"]) and torch.equal(dg, ref["dg"]) and torch.equal(dbeta, ref["dbeta"])
