@@ -159,6 +159,9 @@ gdn_status_t gdn_decode_step(const void* q, const void* k, const void* v,
 
 /*
  * Decode step on a state pool. A padding entry's outputs are written as zeros.
+ * The order of the rows in the pool does not change any result bit; a batch of
+ * at most min(d * d / 16, 512) sequences (512 at d = 128) is worked through in
+ * pool-row order, which streams the rows fastest.
  */
 gdn_status_t gdn_decode_step_slots(const void* q, const void* k, const void* v,
                                    const float* g, const float* beta,

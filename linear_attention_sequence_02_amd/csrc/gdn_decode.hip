@@ -130,9 +130,47 @@ struct ConvPhase {
     }
 };
 
+// Sequences of a slot-indexed batch in the order of their pool rows: the
+// sequence whose key (pool row, then batch position) ranks r-th among the
+// batch's keys. Keys are distinct, so the ranks are a permutation of the
+// batch and every sequence is taken by exactly one rank. Padding entries sort
+// after every pool row. Workgroups that run at the same time then stream
+// state rows that lie close together in the pool; on MI355X that reads and
+// writes the 2 MiB rows of a 384-row pool in random order as fast as in
+// ascending order. Needs num_seqs <= NT (one key per thread) and
+// num_slots < kOrdPadRow.
+constexpr uint32_t kOrdPadRow = (1u << 22) - 1;
+
+template <int NT>
+__device__ __forceinline__ int sequence_of_rank(const int32_t* __restrict__ state_indices,
+                                                int32_t num_slots, int num_seqs, int r, int tid) {
+    __shared__ uint4 s_key4[NT / 4];
+    __shared__ int s_seq;
+    uint32_t* s_key = reinterpret_cast<uint32_t*>(s_key4);
+    uint32_t key = 0xFFFFFFFFu;
+    if (tid < num_seqs) {
+        const int32_t s = state_indices[tid];
+        const uint32_t row = (s >= 0 && s < num_slots) ? static_cast<uint32_t>(s) : kOrdPadRow;
+        key = (row << 9) | static_cast<uint32_t>(tid);
+    }
+    s_key[tid] = key;   // entries past the batch hold the largest key
+    __syncthreads();
+    if (tid < num_seqs) {
+        int rank = 0;
+        for (int j = 0; j < (num_seqs + 3) / 4; ++j) {
+            const uint4 kk = s_key4[j];
+            rank += (kk.x < key) + (kk.y < key) + (kk.z < key) + (kk.w < key);
+        }
+        if (rank == r) s_seq = tid;
+    }
+    __syncthreads();
+    return s_seq;
+}
+
 // CK > 0: q, k and v come from the fused input prologue with K = CK taps (the
-// q, k, v pointers are unused); CK = 0: from the q, k, v arrays.
-template <int D, bool BF16, bool QKN, int CK = 0>
+// q, k, v pointers are unused); CK = 0: from the q, k, v arrays. ORD: a
+// slot-indexed batch taken in pool-row order (sequence_of_rank).
+template <int D, bool BF16, bool QKN, int CK = 0, bool ORD = false>
 __global__ __launch_bounds__(512) void decode_step_kernel(
     const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
@@ -147,9 +185,11 @@ __global__ __launch_bounds__(512) void decode_step_kernel(
     const int tid = threadIdx.x;
     const int c = tid % L;                       // lane within the row group
     const int r0 = tid / L;
-    const int64_t sh = blockIdx.x;               // sequence * num_v_heads + head
-    const int n = static_cast<int>(sh / num_v_heads);
-    const int h = static_cast<int>(sh % num_v_heads);
+    const int h = static_cast<int>(blockIdx.x % num_v_heads);
+    int n = static_cast<int>(blockIdx.x / num_v_heads);
+    if constexpr (ORD)
+        n = sequence_of_rank<NT>(state_indices, num_slots, static_cast<int>(gridDim.x / num_v_heads), n, tid);
+    const int64_t sh = (int64_t)n * num_v_heads + h;   // sequence * num_v_heads + head
     const int hq = h / (num_v_heads / num_qk_heads);
     const int64_t vo_base = sh * D;
 
@@ -481,9 +521,17 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.num_seqs * a.num_v_heads;
     const DecodeConv cv{a.conv_x, a.conv_w, a.conv_in, a.conv_out, a.conv_silu};
     prof::begin(stream, CK > 0 ? "gdn_decode_conv" : "gdn_decode_step");
-    hipLaunchKernelGGL((decode_step_kernel<D, BF16, QKN, CK>), dim3((unsigned)blocks), dim3(NT), 0, stream,
-                       a.q, a.k, a.v, a.g, a.beta, a.state, a.num_qk_heads, a.num_v_heads, a.scale, a.out,
-                       a.state_indices, a.num_slots, cv);
+    bool ordered = false;
+    if constexpr (CK == 0)
+        ordered = a.state_indices != nullptr && a.num_seqs <= NT && (uint32_t)a.num_slots < kOrdPadRow;
+    if (ordered)
+        hipLaunchKernelGGL((decode_step_kernel<D, BF16, QKN, CK, true>), dim3((unsigned)blocks), dim3(NT), 0,
+                           stream, a.q, a.k, a.v, a.g, a.beta, a.state, a.num_qk_heads, a.num_v_heads, a.scale,
+                           a.out, a.state_indices, a.num_slots, cv);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<D, BF16, QKN, CK>), dim3((unsigned)blocks), dim3(NT), 0, stream,
+                           a.q, a.k, a.v, a.g, a.beta, a.state, a.num_qk_heads, a.num_v_heads, a.scale, a.out,
+                           a.state_indices, a.num_slots, cv);
     prof::end(stream);
     return hipGetLastError();
 }

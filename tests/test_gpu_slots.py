@@ -65,6 +65,44 @@ def test_decode_slots(dtype, d):
     _check_pool(pool0, pool.cpu().numpy(), idx, ref_f, TOL[dtype], x.name)
 
 
+@pytest.mark.parametrize("dtype,d,n", [
+    ("bf16", 128, 512),   # 512-thread workgroups: the batch is taken in pool-row order
+    ("bf16", 128, 600),   # more sequences than threads: batch order
+    ("fp32", 64, 256),    # 256-thread workgroups, at the limit
+    ("fp32", 64, 257),
+])
+def test_decode_slots_row_order(dtype, d, n):
+    """A batch in random pool-row order: each workgroup finds its sequence by rank of pool row
+    (up to one sequence per thread of a workgroup) or takes them in batch order (beyond). Either
+    way every sequence must come out bit for bit as the contiguous step computes it from the
+    same state, padding entries give zeros and rows no sequence names stay unchanged."""
+    slots = n + 40
+    rng = np.random.default_rng(n + d)
+    idx = rng.permutation(slots)[:n].astype(np.int32)
+    idx[rng.choice(n, size=5, replace=False)] = [-1, slots, -7, slots + 3, -1]   # padding entries
+    x = I.draw(lengths=[1] * n, hqk=1, hv=2, dk=d, dtype=dtype, seed=70 + d, name=f"decode_row_order_{dtype}_{n}")
+    pool0 = I.state_pool(slots, 2, d, seed=71 + n)
+    dev = to_device(x)
+    pool = torch.from_numpy(pool0).cuda()
+    ti = torch.from_numpy(idx).cuda()
+    valid = (idx >= 0) & (idx < slots)
+    gathered = np.zeros((n,) + pool0.shape[1:], dtype=np.float32)
+    gathered[valid] = pool0[idx[valid]]
+    state = torch.from_numpy(gathered).cuda()
+    log(f"[gpu] gdn_decode_step_slots {x.name} N={n} slots={slots}")
+    out_s = gdn.gdn_decode_step_slots(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], pool, ti, scale=x.scale)
+    out_c = gdn.gdn_decode_step(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], state, scale=x.scale)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    o_s, o_c = out_s.view(bits).cpu().numpy(), out_c.view(bits).cpu().numpy()
+    assert np.array_equal(o_s[valid], o_c[valid]), "outputs differ from the contiguous step"
+    assert not o_s[~valid].any(), "padding entry outputs must be zero"
+    p, st = pool.cpu().numpy(), state.cpu().numpy()
+    assert np.array_equal(p[idx[valid]].view(np.int32), st[valid].view(np.int32)), "states differ"
+    untouched = np.setdiff1d(np.arange(slots), idx[valid])
+    assert np.array_equal(p[untouched].view(np.int32), pool0[untouched].view(np.int32)), "untouched rows changed"
+
+
 @pytest.mark.parametrize("dtype,lengths", [
     ("bf16", [1100, 33, 700, 5]),     # the first and third sequences span several segments
     ("fp32", [70, 33, 130, 5]),
