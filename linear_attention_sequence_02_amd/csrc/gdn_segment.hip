@@ -185,23 +185,40 @@ __device__ __forceinline__ void prod_fetch_gb(ProdRegs& pr, const float* gc, con
     pr.bn = __builtin_bit_cast(float, buf_ld_b32(chunk_rsrc(uniform_ptr(bc), (int64_t)nc * hv * 4), off));
 }
 
-// In-kernel L2 normalisation of one 8-element piece of a k or q row: the 16
-// consecutive lanes that hold the row sum their squares, and each element is
-// scaled and rounded back to bf16 (a zero row stays zero).
-__device__ __forceinline__ u32x4 l2norm_piece(u32x4 x) {
-    float f[8];
+// In-kernel L2 normalisation of N 8-element pieces of k or q rows (a row's 16
+// pieces sit in 16 consecutive lanes): each lane sums its piece's squares, the
+// N row sums are completed over the 16 lanes together (the cross-lane steps of
+// different pieces interleaved, so none waits on its own previous step), and
+// every element is scaled and rounded back to bf16 (a zero row stays zero).
+template <int N>
+__device__ __forceinline__ void l2norm_pieces(u32x4 (&x)[N]) {
+    float ss[N];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        f[2 * j] = __uint_as_float(x[j] << 16);
-        f[2 * j + 1] = __uint_as_float(x[j] & 0xFFFF0000u);
+    for (int p = 0; p < N; ++p) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float lo = __uint_as_float(x[p][j] << 16), hi = __uint_as_float(x[p][j] & 0xFFFF0000u);
+            s = fmaf(lo, lo, s);
+            s = fmaf(hi, hi, s);
+        }
+        ss[p] = s;
     }
-    float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ss = fmaf(f[j], f[j], ss);
-    const float r = rsqrtf(group_sum<16>(ss) + kQkNormEps);
+    for (int p = 0; p < N; ++p) ss[p] += dpp_quad_xor1(ss[p]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = pack_bf16(f[2 * j] * r, f[2 * j + 1] * r);
-    return x;
+    for (int p = 0; p < N; ++p) ss[p] += dpp_quad_xor2(ss[p]);
+#pragma unroll
+    for (int p = 0; p < N; ++p) ss[p] += dpp_half_mirror(ss[p]);
+#pragma unroll
+    for (int p = 0; p < N; ++p) ss[p] += dpp_row_mirror(ss[p]);
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+        const float r = rsqrtf(ss[p] + kQkNormEps);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            x[p][j] = pack_bf16(__uint_as_float(x[p][j] << 16) * r, __uint_as_float(x[p][j] & 0xFFFF0000u) * r);
+    }
 }
 
 // K and Q tiles. Within each 32-key block the keys are held in the
@@ -243,19 +260,28 @@ __device__ __forceinline__ bf16x8 kq_kt_tr(const uint16_t* K, int t, int kk, int
     return __builtin_bit_cast(bf16x8, u);
 }
 
-// Rows past the end of a partial chunk were read as zero.
-template <int MODE>
-__device__ __forceinline__ void prod_stage_kq(SegSmem<MODE>& sm, int buf, const ProdRegs& pr, int pl, bool qk_norm) {
+// Rows past the end of a partial chunk were read as zero. QKN: k (and q) rows
+// are L2-normalised on the way.
+template <int MODE, bool QKN>
+__device__ __forceinline__ void prod_stage_kq(SegSmem<MODE>& sm, int buf, const ProdRegs& pr, int pl) {
+    constexpr int NP = MODE == kModeOut ? 8 : 4;   // pieces 0..3: k; 4..7: q (output pass)
+    u32x4 x[NP];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = pr.k[i];
+        if constexpr (MODE == kModeOut) x[4 + i] = pr.q[i];
+    }
+    if constexpr (QKN) l2norm_pieces<NP>(x);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int p = pl + 256 * i;
         const int row = p >> 4, c8 = p & 15;
-        const u32x4 kv = qk_norm ? l2norm_piece(pr.k[i]) : pr.k[i];
+        const u32x4 kv = x[i];
         const int pr_ = kq_row(row), col = kq_col(c8);
         *reinterpret_cast<u32x2*>(&sm.K[buf][pr_][col]) = u32x2{kv[0], kv[1]};
         *reinterpret_cast<u32x2*>(&sm.K[buf][pr_][col + 8]) = u32x2{kv[2], kv[3]};
         if constexpr (MODE == kModeOut) {
-            const u32x4 qv = qk_norm ? l2norm_piece(pr.q[i]) : pr.q[i];
+            const u32x4 qv = x[4 + i];
             *reinterpret_cast<u32x2*>(&sm.qv.Q[buf][pr_][col]) = u32x2{qv[0], qv[1]};
             *reinterpret_cast<u32x2*>(&sm.qv.Q[buf][pr_][col + 8]) = u32x2{qv[2], qv[3]};
         } else {
@@ -762,10 +788,10 @@ struct SegArgs {
     int32_t num_slots;
     int32_t num_qk_heads, num_v_heads;
     float scale;
-    bool qk_norm;                   // L2-normalise k and q rows as they are staged
 };
 
-template <int MODE>
+// QKN: L2-normalise k and q rows as they are staged.
+template <int MODE, bool QKN>
 __device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A, const SegTask& tk) {
     constexpr int NCW = ChainWaves<MODE>::n;
     const uint16_t* __restrict__ q = A.q;
@@ -815,9 +841,9 @@ __device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A
             fetch_gb(c_begin);
             pr.g = pr.gn;
             pr.b = pr.bn;
-            prod_stage_kq<MODE>(sm, 0, pr, pl, A.qk_norm);
+            prod_stage_kq<MODE, QKN>(sm, 0, pr, pl);
             fetch_kq(clampc(c_begin + 1));
-            if (nchunks > 1) prod_stage_kq<MODE>(sm, 1, pr, pl, A.qk_norm);
+            if (nchunks > 1) prod_stage_kq<MODE, QKN>(sm, 1, pr, pl);
         }
         lds_barrier();
         if (nchunks > 0) {
@@ -837,7 +863,7 @@ __device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A
             if (i + 1 < nchunks)
                 prod_factors<MODE>(sm, (int)((i + 1) % 3), sm.F[(i + 1) & 1], pr, chunk_nc(c + 1), scale, pw,
                                    lane);
-            if (i + 2 < nchunks) prod_stage_kq<MODE>(sm, (int)((i + 2) % 3), pr, pl, A.qk_norm);
+            if (i + 2 < nchunks) prod_stage_kq<MODE, QKN>(sm, (int)((i + 2) % 3), pr, pl);
             fetch_kq(clampc(c + 3));
             pr.g = pr.gn;
             pr.b = pr.bn;
@@ -908,14 +934,15 @@ __device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A
 // Both launches of the segment schedule. Phase 0: segment 0 of every sequence
 // runs the output pass from the initial state (its end state is H_0), and
 // segments 1 .. nseg - 2 build their maps (H from 0, M from I). Phase 1:
-// segments >= 1 run the output pass from the combined entry states.
+// segments >= 1 run the output pass from the combined entry states. QKN: k and
+// q rows are L2-normalised in the kernel.
+template <bool QKN>
 __global__ __launch_bounds__(64 * (4 + kProd)) void segment_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const float* initial_state,
     const int32_t* __restrict__ cu, float* final_state, uint16_t* __restrict__ out, float* __restrict__ segws,
     int64_t total_tokens, int32_t num_seqs, int32_t num_qk_heads, int32_t num_v_heads, int32_t L, int64_t num_segs,
-    float scale, int32_t phase, const int32_t* state_indices, const int32_t* has_initial, int32_t num_slots,
-    int32_t qk_norm) {
+    float scale, int32_t phase, const int32_t* state_indices, const int32_t* has_initial, int32_t num_slots) {
     static_assert(sizeof(SegSmem<kModeHM>) <= sizeof(SegSmem<kModeOut>), "the map pass reuses the output pass's LDS");
     __shared__ SegSmem<kModeOut> sm;
 
@@ -942,12 +969,13 @@ __global__ __launch_bounds__(64 * (4 + kProd)) void segment_kernel(
     tk.c_end = (tk.c_begin + L < nch) ? tk.c_begin + L : nch;
     tk.nchunks = tk.c_end - tk.c_begin;
     const SegArgs A = {q, k, v, g, beta, initial_state, final_state, out, segws, state_indices, has_initial,
-                       num_slots, num_qk_heads, num_v_heads, scale, qk_norm != 0};
+                       num_slots, num_qk_heads, num_v_heads, scale};
     if (phase == 0) {
-        if (tk.j == 0) segment_body<kModeOut>(sm, A, tk);
-        else if (tk.j < tk.nseg - 1) segment_body<kModeHM>(*reinterpret_cast<SegSmem<kModeHM>*>(&sm), A, tk);
+        if (tk.j == 0) segment_body<kModeOut, QKN>(sm, A, tk);
+        else if (tk.j < tk.nseg - 1)
+            segment_body<kModeHM, QKN>(*reinterpret_cast<SegSmem<kModeHM>*>(&sm), A, tk);
     } else if (tk.j > 0) {
-        segment_body<kModeOut>(sm, A, tk);
+        segment_body<kModeOut, QKN>(sm, A, tk);
     }
 }
 
@@ -1104,11 +1132,12 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     // Phase 0 (segment 0's outputs and the other segments' maps) always runs;
     // the combine and phase 1 only when some sequence spans more than one segment.
     const bool multi = a.num_seqs > 1 || a.total_tokens > (int64_t)kChunk * L;
+    auto kern = a.qk_norm ? segment_kernel<true> : segment_kernel<false>;
     prof::begin(stream, multi ? "gdn_segment_maps" : "gdn_segment_out");
-    hipLaunchKernelGGL(segment_kernel, grid, dim3(64 * (4 + kProd)), 0, stream, q, k, v, a.g, a.beta, a.initial_state,
+    hipLaunchKernelGGL(kern, grid, dim3(64 * (4 + kProd)), 0, stream, q, k, v, a.g, a.beta, a.initial_state,
                        a.cu_seqlens, a.final_state, (uint16_t*)a.out, seg_ws, a.total_tokens, a.num_seqs,
                        a.num_qk_heads, a.num_v_heads, L, segs, a.scale, 0, a.state_indices, a.has_initial,
-                       a.num_slots, a.qk_norm ? 1 : 0);
+                       a.num_slots);
     prof::end(stream);
     if (multi) {
         prof::begin(stream, "gdn_segment_combine");
@@ -1116,10 +1145,10 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
                            stream, a.cu_seqlens, seg_ws, a.total_tokens, a.num_seqs, a.num_v_heads, L);
         prof::end(stream);
         prof::begin(stream, "gdn_segment_out");
-        hipLaunchKernelGGL(segment_kernel, grid, dim3(64 * (4 + kProd)), 0, stream, q, k, v, a.g, a.beta,
+        hipLaunchKernelGGL(kern, grid, dim3(64 * (4 + kProd)), 0, stream, q, k, v, a.g, a.beta,
                            a.initial_state, a.cu_seqlens, a.final_state, (uint16_t*)a.out, seg_ws, a.total_tokens,
                            a.num_seqs, a.num_qk_heads, a.num_v_heads, L, segs, a.scale, 1, a.state_indices,
-                           a.has_initial, a.num_slots, a.qk_norm ? 1 : 0);
+                           a.has_initial, a.num_slots);
         prof::end(stream);
     }
     return hipGetLastError();
