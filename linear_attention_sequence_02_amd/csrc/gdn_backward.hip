@@ -720,19 +720,25 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
             if (rb + 1 < NB) load_block(rb + 1);
         }
         mf::lds_barrier();
-        // K S0^T and K G^T for the block's columns: 2 NTR tiles.
-        for (int tile = w; tile < 2 * NTR; tile += 4) {
-            const float (*B)[KP] = tile < NTR ? Sb : Gb;
-            const int nt = tile % NTR;
+        // K S0^T (waves 0, 2) and K G^T (waves 1, 3) for the block's 16 columns, each wave over
+        // one half of the d keys (two chains of D / 8 steps instead of one of D / 4 on two
+        // waves). The second halves go to Rs and dUs, which are written only after those
+        // halves are read (by the same wave, same elements), and are added where read.
+        {
+            static_assert(NTR == 1, "one 16-column tile per block");
+            const float (*B)[KP] = (w & 1) ? Gb : Sb;
+            const int k0 = (w >> 1) * (D / 8);
             f32x4 acc = zero4;
-            for (int kk = 0; kk < D / 4; ++kk) {
+            for (int kk = k0; kk < k0 + D / 8; ++kk) {
                 const int k = 4 * kk + g4;
-                acc = mfma4(Kf[m][k], B[16 * nt + m][k], acc);
+                acc = mfma4(Kf[m][k], B[m][k], acc);
             }
-            float (*dst)[BP] = tile < NTR ? KSs : KGs;
+            float (*dst)[BP] = w == 0 ? KSs : w == 1 ? KGs : w == 2 ? Rs : dUs;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[4 * g4 + e][16 * nt + m] = acc[e];
+            for (int e = 0; e < 4; ++e) dst[4 * g4 + e][m] = acc[e];
         }
+        float (*KSh)[BP] = Rs;    // K S0^T, second half of the keys
+        float (*KGh)[BP] = dUs;   // K G^T, second half of the keys
         mf::lds_barrier();
         // U (waves 0 .. NTR - 1) and Z = P^T dO (waves 2 .. 2 + NTR - 1).
         if (w < NTR) {
@@ -741,7 +747,7 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int k = 4 * kk + g4;
-                acc = mfma4(Tm[m][k], bet[k] * (Vb[k][c] - Gam[k] * KSs[k][c]), acc);
+                acc = mfma4(Tm[m][k], bet[k] * (Vb[k][c] - Gam[k] * (KSs[k][c] + KSh[k][c])), acc);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) Us[4 * g4 + e][c] = acc[e];
@@ -756,7 +762,7 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 4 * g4 + e;
-                KGs[t][c] = fmaf(Gp[t], KGs[t][c], scale * acc[e]);   // Y = Gp K G^T + scale P^T dO
+                KGs[t][c] = fmaf(Gp[t], KGs[t][c] + KGh[t][c], scale * acc[e]);   // Y = Gp K G^T + scale P^T dO
             }
         }
         // Each wave next reads only the columns of U (or Y) it has just written.
@@ -773,7 +779,7 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 4 * g4 + e;
-                Rs[t][c] = Vb[t][c] - fmaf(Gam[t], KSs[t][c], acc[e]);
+                Rs[t][c] = Vb[t][c] - fmaf(Gam[t], KSs[t][c] + KSh[t][c], acc[e]);
             }
         } else if (w >= 2 && w < 2 + NTR) {
             const int c = 16 * (w - 2) + m;
