@@ -19,7 +19,7 @@
 //     S_after  = exp(gamma_last) S0 + (diag(Gp) U)^T K
 //     G_before = exp(gamma_last) G + (scale diag(Gam) dO)^T Q - (diag(Gam beta) dU)^T K
 // The passes:
-//   1. prep, every (chunk, V head) in parallel: gamma, beta, At, P and T;
+//   1. prep, every (chunk, QK head) in parallel: gamma, beta, At, P and T of its V heads;
 //   2. scans, per (sequence, V head, 16 state rows) and direction, chunk by
 //      chunk: S0 of every chunk (forward) and G of every chunk (reverse, and the
 //      gradient of the initial state);
@@ -180,14 +180,16 @@ struct alignas(16) ChunkFac {
     float At[kC][kC];         // exp(gamma_r - gamma_c) (k_r . k_c), c < r
 };
 
-// Pass 1: one wave per (slot, V head).
+// Pass 1: one wave per (slot, QK head): K, Q and their Gram products (K K^T,
+// Q K^T) once, then the decay-masked factors of each V head of the QK head,
+// four V heads at a time (lanes 16 x .. 16 x + 15 take V head x0 + x).
 template <int D, bool BF16>
 __global__ __launch_bounds__(64) void backward_prep_kernel(BwdIn in, ChunkFac* __restrict__ fac) {
     constexpr int KP = D + 4;
     __shared__ __align__(16) float Kf[kC][KP], Qf[kC][KP];
-    __shared__ float gin[kC], bet[kC], gam[kC], At[kC][kC + 1];
-    const int hv = in.num_v_heads, h = blockIdx.x % hv, hq = h / (hv / in.num_qk_heads);
-    const int64_t sl = blockIdx.x / hv;
+    __shared__ float gin[4][kC], bet[4][kC], gam[4][kC], At[4][kC][kC + 1];
+    const int hv = in.num_v_heads, hqk = in.num_qk_heads, hq = blockIdx.x % hqk, group = hv / hqk;
+    const int64_t sl = blockIdx.x / hqk;
     int n, cnt;
     int64_t t0;
     if (!slot_chunk(in, sl, n, t0, cnt)) return;
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(64) void backward_prep_kernel(BwdIn in, ChunkFac* _
     constexpr int NE = D / 16;
     for (int e = ln; e < kC * 16; e += 64) {
         const int t = e / 16, c = NE * (e % 16);
-        const int64_t idx = ((t0 + min(t, cnt - 1)) * in.num_qk_heads + hq) * D + c;
+        const int64_t idx = ((t0 + min(t, cnt - 1)) * hqk + hq) * D + c;
         const float keep = t < cnt ? 1.f : 0.f;
         float kv[NE], qv[NE];
         ld_vec<BF16, NE>(in.k, idx, kv);
@@ -207,18 +209,7 @@ __global__ __launch_bounds__(64) void backward_prep_kernel(BwdIn in, ChunkFac* _
             Qf[t][c + i] = keep * qv[i];
         }
     }
-    if (ln < kC) {
-        const int64_t gi = (t0 + min(ln, cnt - 1)) * hv + h;
-        const float keep = ln < cnt ? 1.f : 0.f;
-        gin[ln] = keep * in.g[gi];
-        bet[ln] = keep * in.beta[gi];
-    }
     __syncthreads();
-    if (ln < kC) {
-        float s = 0.f;
-        for (int t = 0; t <= ln; ++t) s += gin[t];
-        gam[ln] = s;
-    }
     f32x4 kk_ = {0.f, 0.f, 0.f, 0.f}, qk_ = kk_;
     for (int kk = 0; kk < D / 4; ++kk) {
         const int k = 4 * kk + g4;
@@ -226,38 +217,62 @@ __global__ __launch_bounds__(64) void backward_prep_kernel(BwdIn in, ChunkFac* _
         kk_ = mfma4(kv, kv, kk_);
         qk_ = mfma4(Qf[m][k], kv, qk_);
     }
-    __syncthreads();
-    ChunkFac& F = fac[sl * hv + h];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g4 + e, c = m;
-        const float dec = exp_nonpos(fminf(gam[r] - gam[c], 0.f));
-        const float at = c < r ? dec * kk_[e] : 0.f;
-        At[r][c] = at;
-        F.At[r][c] = at;
-        F.P[r][c] = c <= r ? dec * qk_[e] : 0.f;
-    }
-    if (ln < kC) {
-        F.gam[ln] = gam[ln];
-        F.bet[ln] = bet[ln];
-        F.Gam[ln] = exp_nonpos(gam[ln]);
-        F.Gp[ln] = exp_nonpos(gam[kC - 1] - gam[ln]);
-    }
-    __syncthreads();
-    // T by forward substitution, lane c solving column c.
-    if (ln < kC) {
-        const int c = ln;
-        float Tc[kC];
-#pragma unroll
-        for (int r = 0; r < kC; ++r) {
-            float s = r == c ? 1.f : 0.f;
-            const float br = bet[r];
-#pragma unroll
-            for (int p = 0; p < r; ++p) s = fmaf(-br * At[r][p], Tc[p], s);
-            Tc[r] = s;
+    // Lane (x, c) of a round: V head x0 + x, token (or column) c.
+    const int x = ln / 16, c16 = ln % 16;
+    for (int x0 = 0; x0 < group; x0 += 4) {
+        const bool mine = x0 + x < group;
+        const int hx = hq * group + x0 + x;   // this lane's V head (if mine)
+        if (mine) {
+            const int64_t gi = (t0 + min(c16, cnt - 1)) * hv + hx;
+            const float keep = c16 < cnt ? 1.f : 0.f;
+            gin[x][c16] = keep * in.g[gi];
+            bet[x][c16] = keep * in.beta[gi];
         }
+        __syncthreads();
+        if (mine) {
+            float s = 0.f;
+            for (int t = 0; t <= c16; ++t) s += gin[x][t];
+            gam[x][c16] = s;
+        }
+        __syncthreads();
+        // At and P of every V head of the round, from the Gram tiles in this lane's registers.
+        for (int xx = 0; xx < 4 && x0 + xx < group; ++xx) {
+            ChunkFac& F = fac[sl * hv + hq * group + x0 + xx];
 #pragma unroll
-        for (int r = 0; r < kC; ++r) F.T[r][c] = Tc[r];
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g4 + e, c = m;
+                const float dec = exp_nonpos(fminf(gam[xx][r] - gam[xx][c], 0.f));
+                const float at = c < r ? dec * kk_[e] : 0.f;
+                At[xx][r][c] = at;
+                F.At[r][c] = at;
+                F.P[r][c] = c <= r ? dec * qk_[e] : 0.f;
+            }
+        }
+        if (mine) {
+            ChunkFac& F = fac[sl * hv + hx];
+            F.gam[c16] = gam[x][c16];
+            F.bet[c16] = bet[x][c16];
+            F.Gam[c16] = exp_nonpos(gam[x][c16]);
+            F.Gp[c16] = exp_nonpos(gam[x][kC - 1] - gam[x][c16]);
+        }
+        __syncthreads();
+        // T by forward substitution, lane (x, c) solving column c of V head x0 + x.
+        if (mine) {
+            ChunkFac& F = fac[sl * hv + hx];
+            const int c = c16;
+            float Tc[kC];
+#pragma unroll
+            for (int r = 0; r < kC; ++r) {
+                float s = r == c ? 1.f : 0.f;
+                const float br = bet[x][r];
+#pragma unroll
+                for (int p = 0; p < r; ++p) s = fmaf(-br * At[x][r][p], Tc[p], s);
+                Tc[r] = s;
+            }
+#pragma unroll
+            for (int r = 0; r < kC; ++r) F.T[r][c] = Tc[r];
+        }
+        __syncthreads();   // the round's LDS is reused by the next
     }
 }
 
@@ -999,7 +1014,8 @@ static hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t stream) {
     hipError_t e;
     if (a.total_tokens > 0) {
         prof::begin(stream, "gdn_backward_prep");
-        hipLaunchKernelGGL((backward_prep_kernel<D, BF16>), dim3(chunks), dim3(64), 0, stream, in, fac);
+        hipLaunchKernelGGL((backward_prep_kernel<D, BF16>), dim3((unsigned)(slots * a.num_qk_heads)), dim3(64), 0,
+                           stream, in, fac);
         prof::end(stream);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
