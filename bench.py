@@ -757,14 +757,16 @@ def main():
 
         bsteps = max(2, args.steps // 4)
         bms, bkern = time_calls(backward, bsteps, 2, torch, warm_s=0.3)
-        # four stages per call: chunk factors, the two scans, the per-chunk gradients, the fixed-order sums
+        # stages per call: chunk factors, the two scans, the per-chunk gradients (at 16 / 32 heads the
+        # two V heads of a QK head add into dq, dk there; with three or more, a fixed-order sums launch)
         bparts = {k: bkern[k][1] for k in ("gdn_backward_prep", "gdn_backward_scan", "gdn_backward_grad",
                                             "gdn_backward_sums") if k in bkern}
         bkms = sum(bparts.values()) or bms
         btf = BACKWARD_FLOP_PER_TOKEN * xb.T / (bkms / 1e3) / 1e12
         result["backward"] = {"workload": "qwen3next_gdn_backward_T4096", "steps": bsteps, "ms_per_step": bms,
                               "kernel_ms_per_launch": bparts, "tokens_per_s": xb.T / (bms / 1e3),
-                              "roofline": {"kernel": "gdn_backward_prep+scan+grad+sums", "bound": "mfma",
+                              "roofline": {"kernel": "+".join(k.replace("gdn_backward_", "gdn_backward_" if i == 0 else "")
+                                                           for i, k in enumerate(bparts)), "bound": "mfma",
                                            "achieved": btf,
                                            "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                                            "frac": btf / PEAK_FP32_MFMA_TFLOPS}}

@@ -283,8 +283,10 @@ gdn_status_t gdn_decode_ex(const void* q, const void* k, const void* v,
  * MFMA): a pass builds every chunk's factors, two scans (forward and reverse,
  * 16 state rows per workgroup) store the state before and the state gradient
  * after every chunk in the workspace, every chunk's gradients then follow in
- * parallel from those two, and a last pass sums dq and dk over the V heads of
- * each QK head in a fixed order, so results are deterministic.
+ * parallel from those two. dq and dk of a QK head are formed from its V heads'
+ * shares deterministically: one V head stores its share, two add theirs into
+ * the output zeroed beforehand (0 + a + b and 0 + b + a are the same float),
+ * three or more are summed by a last pass in a fixed order.
  * workspace: gdn_backward_workspace_size(...) bytes, for d = d_k = d_v:
  * 8 d^2 Hv (T / 16 + N) + 8 d Hv T + 3328 Hv (T / 16 + N).
  */

@@ -24,8 +24,11 @@
 //      chunk: S0 of every chunk (forward) and G of every chunk (reverse, and the
 //      gradient of the initial state);
 //   3. gradients, every (chunk, V head) in parallel, in closed form from S0 and G;
-//   4. dq and dk summed over the V heads of each QK head in a fixed order, so
-//      results are deterministic.
+//   4. dq and dk of each QK head from its V heads' shares, deterministically: one V
+//      head stores its share; two add theirs into the output that pass 1 zeroed
+//      (0 + a + b and 0 + b + a are the same float under IEEE addition, and also
+//      when subnormal operands are flushed); three or more write their shares to the
+//      workspace, which a last launch sums in a fixed order.
 // Every product is fp32 MFMA 16x16x4: lane (g, m) = (lane / 16, lane % 16) gives
 // A[m][k] and B[k][m] for the step's k and receives D[4 g + e][m], e = 0..3.
 // Steps take k = 4 kk + g, which spreads a row-major operand's reads over the
@@ -39,6 +42,14 @@ namespace gdn {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kC = 16;   // tokens per chunk; also the checkpoint interval
 
+// How dq and dk of a QK head are formed from its V heads' shares:
+enum DqkMode {
+    kDqkPartial = 0,   // per V head into the workspace, then summed in a fixed order (pass 4)
+    kDqkDirect = 1,    // one V head per QK head: stored directly
+    kDqkPair = 2,      // two V heads: each adds its share into the output, zeroed by pass 1; with
+                       // exactly two addends on 0 the sum does not depend on their order
+};
+
 struct BwdIn {
     const void *q, *k, *v, *dout;
     const float *g, *beta;
@@ -46,6 +57,8 @@ struct BwdIn {
     int64_t total_tokens;
     int32_t num_seqs, num_qk_heads, num_v_heads;
     float scale;
+    float *dq, *dk;    // the outputs [T, Hqk, d]
+    int32_t dqk_mode;  // DqkMode
 };
 
 // Slot of chunk j of sequence n: cu[n] / 16 + n + j. The ranges of different
@@ -194,6 +207,22 @@ __global__ __launch_bounds__(64) void backward_prep_kernel(BwdIn in, ChunkFac* _
     int64_t t0;
     if (!slot_chunk(in, sl, n, t0, cnt)) return;
     const int ln = threadIdx.x, g4 = ln / 16, m = ln % 16;
+    if (in.dqk_mode == kDqkPair) {   // the chunk's dq and dk rows of this QK head start at 0
+        if (((reinterpret_cast<uintptr_t>(in.dq) | reinterpret_cast<uintptr_t>(in.dk)) & 15) == 0) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            for (int e = ln; e < cnt * (D / 4); e += 64) {
+                const int64_t gi = ((t0 + e / (D / 4)) * hqk + hq) * D + 4 * (e % (D / 4));
+                *reinterpret_cast<f32x4*>(in.dq + gi) = z;
+                *reinterpret_cast<f32x4*>(in.dk + gi) = z;
+            }
+        } else {
+            for (int e = ln; e < cnt * D; e += 64) {
+                const int64_t gi = ((t0 + e / D) * hqk + hq) * D + e % D;
+                in.dq[gi] = 0.f;
+                in.dk[gi] = 0.f;
+            }
+        }
+    }
     // K and Q rows in pieces of D / 16 elements (the scan reads its rows in the same pieces).
     constexpr int NE = D / 16;
     for (int e = ln; e < kC * 16; e += 64) {
@@ -947,9 +976,20 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
             for (int e = 0; e < 4; ++e) {
                 const int t = 4 * g4 + e;
                 if (t < cnt) {
-                    const int64_t gi = ((t0 + t) * hv + h) * D + col;
-                    dq_h[gi] = scale * q_[e];
-                    dk_h[gi] = k_[e];
+                    if (in.dqk_mode == kDqkPartial) {
+                        const int64_t gi = ((t0 + t) * hv + h) * D + col;
+                        dq_h[gi] = scale * q_[e];
+                        dk_h[gi] = k_[e];
+                    } else {
+                        const int64_t gi = ((t0 + t) * hqk + hq) * D + col;
+                        if (in.dqk_mode == kDqkDirect) {
+                            in.dq[gi] = scale * q_[e];
+                            in.dk[gi] = k_[e];
+                        } else {
+                            unsafeAtomicAdd(in.dq + gi, scale * q_[e]);
+                            unsafeAtomicAdd(in.dk + gi, k_[e]);
+                        }
+                    }
                 }
             }
         }
@@ -1008,8 +1048,10 @@ static hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t stream) {
     float* dq_h = ck_ds + ck;
     float* dk_h = dq_h + qk;
     ChunkFac* fac = reinterpret_cast<ChunkFac*>(dk_h + qk);
+    const int group = a.num_v_heads / a.num_qk_heads;
+    const int32_t mode = group == 1 ? kDqkDirect : group == 2 ? kDqkPair : kDqkPartial;
     const BwdIn in{a.q, a.k, a.v, a.d_out, a.g, a.beta, a.cu_seqlens, a.total_tokens,
-                   a.num_seqs, a.num_qk_heads, a.num_v_heads, a.scale};
+                   a.num_seqs, a.num_qk_heads, a.num_v_heads, a.scale, a.dq, a.dk, mode};
     const unsigned chunks = (unsigned)(slots * a.num_v_heads);
     hipError_t e;
     if (a.total_tokens > 0) {
@@ -1030,8 +1072,8 @@ static hipError_t launch_bwd_t(const BackwardArgs& a, hipStream_t stream) {
                        dq_h, dk_h, a.dg, a.dbeta, a.dv);
     prof::end(stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (mode != kDqkPartial) return hipSuccess;
     const int64_t nqk = a.total_tokens * a.num_qk_heads * D;
-    const int group = a.num_v_heads / a.num_qk_heads;
     prof::begin(stream, "gdn_backward_sums");
     const bool aligned = ((reinterpret_cast<uintptr_t>(dq_h) | reinterpret_cast<uintptr_t>(dk_h) |
                            reinterpret_cast<uintptr_t>(a.dq) | reinterpret_cast<uintptr_t>(a.dk)) & 15) == 0;

@@ -113,12 +113,14 @@ def test_backward_no_tokens():
         assert res[name].shape[0] == 0
 
 
-def test_backward_unaligned_dq_dk():
-    """dq and dk at addresses that are not 16-byte aligned take the one-element-per-thread sums;
-    they add the V heads' parts in the same order as the 16-byte path, so the results are the same
-    bits as with aligned outputs (the layer's 16 QK / 32 V heads, d = 128, a ragged length)."""
-    x = I.draw(lengths=[150], hqk=16, hv=32, dk=128, dtype="bf16", seed=451, s0_std=0.1,
-               scale=128 ** -0.5, name="backward_unaligned")
+@pytest.mark.parametrize("hqk,hv", [(16, 32), (4, 12)])
+def test_backward_unaligned_dq_dk(hqk, hv):
+    """dq and dk at addresses that are not 16-byte aligned give the same bits as aligned outputs
+    (d = 128, a ragged length). With two V heads per QK head (the layer's 16 / 32) both add their
+    shares into the output; with three (4 / 12) the shares are summed by the one-element-per-thread
+    launch, in the same order as the 16-byte one."""
+    x = I.draw(lengths=[150], hqk=hqk, hv=hv, dk=128, dtype="bf16", seed=451, s0_std=0.1,
+               scale=128 ** -0.5, name=f"backward_unaligned_{hqk}_{hv}")
     rng = np.random.default_rng(452)
     dev = to_device(x)
     d_out = torch.from_numpy(I.f32_to_bf16_bits(rng.standard_normal(x.v.shape).astype(np.float32))).view(
@@ -146,3 +148,53 @@ def test_backward_unaligned_dq_dk():
     assert torch.equal(dq_buf[1:].view(T, hqk, d), ref["dq"])
     assert torch.equal(dk_buf[1:].view(T, hqk, d), ref["dk"])
     assert torch.equal(dv, ref["dv"]) and torch.equal(dg, ref["dg"]) and torch.equal(dbeta, ref["dbeta"])
+
+
+@pytest.mark.parametrize("dtype,d,hqk,hv", [
+    ("fp32", 32, 2, 2),     # one V head per QK head: dq, dk stored directly
+    ("fp32", 32, 1, 3),     # three: shares summed in a fixed order by a last launch
+    ("bf16", 128, 2, 4),    # two: both shares added into the zeroed output
+])
+def test_backward_head_groups(dtype, d, hqk, hv):
+    """Each way of forming dq and dk from the V heads that share a QK head, against the oracle."""
+    lengths = [70, 0, 33]
+    x = I.draw(lengths=lengths, hqk=hqk, hv=hv, dk=d, dtype=dtype, seed=460 + hv, s0_std=0.3, scale=0.5,
+               name=f"backward_groups_{hqk}_{hv}")
+    rng = np.random.default_rng(461 + hv)
+    d_out = rng.standard_normal(x.v.shape).astype(np.float32)
+    d_fin = rng.standard_normal(x.s0.shape).astype(np.float32)
+    if dtype == "bf16":
+        d_out_in = I.f32_to_bf16_bits(d_out)
+        d_out = oracle.upcast(d_out_in)
+        dev_dout = torch.from_numpy(d_out_in).view(torch.bfloat16).cuda()
+    else:
+        dev_dout = torch.from_numpy(d_out).cuda()
+    dev = to_device(x)
+    log(f"[gpu] gdn_backward {x.name} T={x.T} heads {hqk}/{hv}")
+    res = gdn.gdn_backward(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev_dout, dev["s0"], dev["cu"],
+                           torch.from_numpy(d_fin).cuda(), scale=x.scale)
+    torch.cuda.synchronize()
+    ref = oracle.backward(x.q, x.k, x.v, x.g, x.beta, x.s0, x.cu_seqlens, d_out, d_fin, scale=x.scale)
+    for mine, theirs in [("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dg", "dg"), ("dbeta", "dbeta"),
+                         ("d_initial_state", "ds0")]:
+        e = rel_l2(res[mine].cpu().numpy(), ref[theirs])
+        log(f"[parity] {x.name} {mine}: rel={e:.3e}")
+        assert e <= TOL, (mine, e)
+
+
+def test_backward_deterministic():
+    """Three calls on the layer's head layout (two V heads add into each QK head's dq, dk) give the
+    same bits."""
+    x = I.draw(lengths=[700, 333], hqk=16, hv=32, dk=128, dtype="bf16", seed=471, s0_std=0.1,
+               scale=128 ** -0.5, name="backward_deterministic")
+    rng = np.random.default_rng(472)
+    d_out = torch.from_numpy(I.f32_to_bf16_bits(rng.standard_normal(x.v.shape).astype(np.float32))).view(
+        torch.bfloat16).cuda()
+    dev = to_device(x)
+    log(f"[gpu] gdn_backward {x.name} T={x.T}, three calls")
+    runs = [gdn.gdn_backward(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], d_out, dev["s0"], dev["cu"],
+                             scale=x.scale) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for name in ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state"):
+            assert torch.equal(r[name], runs[0][name]), name
