@@ -328,7 +328,7 @@ struct ScanSmem {
     static constexpr int KP = D + 4, SP = kC + 1;
     float Kc[3][kC][KP], Qc[3][kC][KP];
     float Xc[3][kC][SP], Tc[3][kC][SP], Pc[3][kC][SP], Gc[3][kC], Hc[3][kC], bc[3][kC];   // Hc: Gp
-    float part[2][4][kC][SP], Uw[4][kC][SP];
+    float part[2][4][kC][SP];
 };
 
 // One direction's scan (REV: the gradient, in reverse); b indexes (sequence, V head, value tile).
@@ -352,7 +352,6 @@ __device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, cons
     auto& Hc = sm.Hc;
     auto& bc = sm.bc;
     auto& part = sm.part;
-    auto& Uw = sm.Uw;
     const int hv = in.num_v_heads, hqk = in.num_qk_heads;
     const int vt = (int)(b % NTD);
     const int nh = (int)(b / NTD);
@@ -500,20 +499,22 @@ __device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, cons
         }
         if (q + 4 < nint) fetch(pre, q + 4);
         const float GL = Gc[bb][kC - 1];   // exp(gamma_last)
-        // The update's K (and Q) operands, read with the phase's other operands.
+        // The update's K (and Q) operands, read with the phase's other operands. The update takes
+        // its reduction index (the token) in the order 4 g + kk, the row order of an accumulator
+        // tile, so that U (forward) or dU (reverse) enters it straight from its accumulator.
         float ku[TPW][4], qu[TPW][4];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int tk = w + 4 * i;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const int tau = 4 * kk + g4;
+                const int tau = 4 * g4 + kk;
                 ku[i][kk] = (kAllTiles || tk < NTD) ? Kc[bb][tau][16 * tk + m] : 0.f;
                 if constexpr (REV) qu[i][kk] = (kAllTiles || tk < NTD) ? Qc[bb][tau][16 * tk + m] : 0.f;
             }
         }
         if constexpr (!REV) {
-            // U = T diag(beta) (V - diag(Gam) K S0^T), then Gp U to this wave's LDS rows.
+            // U = T diag(beta) (V - diag(Gam) K S0^T); its accumulator scaled by Gp is the update's operand.
             float pr[4][4], xr[4], gr[4], br[4], tr[4], hr[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -533,14 +534,10 @@ __device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, cons
                 const float ks = (pr[kk][0] + pr[kk][1]) + (pr[kk][2] + pr[kk][3]);
                 u = mfma4(tr[kk], br[kk] * (xr[kk] - gr[kk] * ks), u);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Uw[w][4 * g4 + e][m] = hr[e] * u[e];
-            wave_lds_sync();
             // S^T <- exp(gamma_last) S^T + K^T (Gp U)
             float uu[4];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) uu[kk] = Uw[w][4 * kk + g4][m];
-            __builtin_amdgcn_sched_barrier(0);
+            for (int kk = 0; kk < 4; ++kk) uu[kk] = hr[kk] * u[kk];
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
                 const int tk = w + 4 * i;
@@ -552,7 +549,9 @@ __device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, cons
                 }
             }
         } else {
-            // Y = Gp K G^T + scale Z, dU = T^T Y, then -Gam beta dU to this wave's LDS rows.
+            // Y = Gp K G^T + scale Z, dU = T^T Y, then -Gam beta dU. Every product here takes its
+            // reduction index in the order 4 g + kk, so Y and dU pass from one product to the next
+            // in registers: lane (g, m) holds rows 4 g .. 4 g + 3 of column m of each.
             float pr[4][4], hr[4], gr[4], br[4], tt[4], gx[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -562,33 +561,23 @@ __device__ __forceinline__ void scan_body(ScanSmem<D>& sm, const BwdIn& in, cons
                 hr[e] = Hc[bb][tau];
                 gr[e] = Gc[bb][tau];
                 br[e] = bc[bb][tau];
-                const int tk4 = 4 * e + g4;   // reduction index of the products below
-                tt[e] = Tc[bb][tk4][m];
-                gx[e] = scale * Gc[bb][tk4] * Xc[bb][tk4][m];
+                tt[e] = Tc[bb][tau][m];
+                gx[e] = scale * Gc[bb][tau] * Xc[bb][tau][m];
             }
             __builtin_amdgcn_sched_barrier(0);
+            float y[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float kg = (pr[e][0] + pr[e][1]) + (pr[e][2] + pr[e][3]);
-                Uw[w][4 * g4 + e][m] = fmaf(hr[e], kg, scale * zkeep[e]);
+                y[e] = fmaf(hr[e], kg, scale * zkeep[e]);
             }
-            wave_lds_sync();
-            float y[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) y[kk] = Uw[w][4 * kk + g4][m];
-            __builtin_amdgcn_sched_barrier(0);
             f32x4 du = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) du = mfma4(tt[kk], y[kk], du);
-            wave_lds_sync();
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Uw[w][4 * g4 + e][m] = -gr[e] * br[e] * du[e];
-            wave_lds_sync();
             // G^T <- exp(gamma_last) G^T + Q^T (scale Gam dO) + K^T (-Gam beta dU)
             float uu[4];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) uu[kk] = Uw[w][4 * kk + g4][m];
-            __builtin_amdgcn_sched_barrier(0);
+            for (int kk = 0; kk < 4; ++kk) uu[kk] = -gr[kk] * br[kk] * du[kk];
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
                 const int tk = w + 4 * i;
