@@ -177,12 +177,6 @@ __device__ __forceinline__ float swap32_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS written by some lanes of a wave and then read by others of the same wave.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Per (chunk slot, V head): the chunk's factors.
 struct alignas(16) ChunkFac {
@@ -773,42 +767,22 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
         float (*KSh)[BP] = Rs;    // K S0^T, second half of the keys
         float (*KGh)[BP] = dUs;   // K G^T, second half of the keys
         mf::lds_barrier();
-        // U (waves 0 .. NTR - 1) and Z = P^T dO (waves 2 .. 2 + NTR - 1).
+        // U, then AW = Gam K S0^T + At U and R = V - AW (wave 0); Z = P^T dO, Y = Gp K G^T + scale Z,
+        // then dU = T^T Y (wave 2). The second product of each takes its reduction index in the
+        // order 4 g + kk, the row order of an accumulator tile, so U and Y reach it in registers.
         if (w < NTR) {
             const int c = 16 * w + m;
-            f32x4 acc = zero4;
+            f32x4 u = zero4;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int k = 4 * kk + g4;
-                acc = mfma4(Tm[m][k], bet[k] * (Vb[k][c] - Gam[k] * (KSs[k][c] + KSh[k][c])), acc);
+                u = mfma4(Tm[m][k], bet[k] * (Vb[k][c] - Gam[k] * (KSs[k][c] + KSh[k][c])), u);
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Us[4 * g4 + e][c] = acc[e];
-        } else if (w >= 2 && w < 2 + NTR) {
-            const int c = 16 * (w - 2) + m;
+            for (int e = 0; e < 4; ++e) Us[4 * g4 + e][c] = u[e];
             f32x4 acc = zero4;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int k = 4 * kk + g4;
-                acc = mfma4(Pm[k][m], dOb[k][c], acc);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 4 * g4 + e;
-                KGs[t][c] = fmaf(Gp[t], KGs[t][c] + KGh[t][c], scale * acc[e]);   // Y = Gp K G^T + scale P^T dO
-            }
-        }
-        // Each wave next reads only the columns of U (or Y) it has just written.
-        wave_lds_sync();
-        // AW = Gam K S0^T + At U, R = V - AW (waves 0 ..); dU = T^T Y (waves 2 ..).
-        if (w < NTR) {
-            const int c = 16 * w + m;
-            f32x4 acc = zero4;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int k = 4 * kk + g4;
-                acc = mfma4(At[m][k], Us[k][c], acc);
-            }
+            for (int kk = 0; kk < 4; ++kk) acc = mfma4(At[m][4 * g4 + kk], u[kk], acc);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 4 * g4 + e;
@@ -816,12 +790,21 @@ __global__ __launch_bounds__(256) void backward_grad_kernel(
             }
         } else if (w >= 2 && w < 2 + NTR) {
             const int c = 16 * (w - 2) + m;
-            f32x4 acc = zero4;
+            f32x4 z = zero4;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const int k = 4 * kk + g4;
-                acc = mfma4(Tm[k][m], KGs[k][c], acc);
+                z = mfma4(Pm[k][m], dOb[k][c], z);
             }
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * g4 + e;
+                y[e] = fmaf(Gp[t], KGs[t][c] + KGh[t][c], scale * z[e]);   // Y = Gp K G^T + scale P^T dO
+            }
+            f32x4 acc = zero4;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mfma4(Tm[4 * g4 + kk][m], y[kk], acc);
 #pragma unroll
             for (int e = 0; e < 4; ++e) dUs[4 * g4 + e][c] = acc[e];
         }
