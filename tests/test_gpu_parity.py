@@ -330,6 +330,29 @@ def test_prefill_long_carry_no_decay(dtype):
     _check(x, out, fin, TOL_BF16 if dtype == "bf16" else TOL_FP32, TOL_BF16_SLICE if dtype == "bf16" else None)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_prefill_degenerate_gates_and_boundaries(dtype):
+    """The gates at their limits and lengths at the chunk and segment boundaries, against the oracle:
+    stretches of tokens with g = -30 (alpha = 9e-14: the state is all but reset at every token),
+    g = 0 (no decay), beta = 0 (no write), beta = 1 (full replacement along the key), zero keys and
+    zero queries; sequence lengths 64, 1, 63, 65, 512 (one whole segment of 8 chunks here), 513,
+    1024 and 0, with initial states."""
+    lengths = [64, 1, 63, 65, 512, 513, 1024, 0]
+    x = I.draw(lengths=lengths, hqk=2, hv=4, dk=128, dtype=dtype, seed=91, s0_std=0.3,
+               name=f"{dtype}_degenerate_gates")
+    T = x.T
+    t = np.arange(T)
+    x.g[(t % 97) < 9] = -30.0
+    x.g[(t % 89) > 79] = 0.0
+    x.beta[(t % 83) < 7] = 0.0
+    x.beta[(t % 79) > 70] = 1.0
+    x.k[(t % 101) < 3] = 0
+    x.q[(t % 103) < 3] = 0
+    assert T == sum(lengths)
+    out, fin = run_prefill(x)
+    _check(x, out, fin, TOL_BF16 if dtype == "bf16" else TOL_FP32, TOL_BF16_SLICE if dtype == "bf16" else None)
+
+
 def test_prefill_bf16_pure_decay_closed_form():
     # beta = 0: o_t = exp(sum_{s<=t} g_s) S0 q_t, S_T = exp(sum g) S0 (no oracle involved).
     x = I.draw(lengths=[333], hqk=1, hv=2, dk=128, dtype="bf16", seed=83, s0_std=1.0, g_mean=-6.0,
