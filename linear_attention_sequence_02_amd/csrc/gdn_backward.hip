@@ -177,7 +177,6 @@ __device__ __forceinline__ float swap32_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-
 // Per (chunk slot, V head): the chunk's factors.
 struct alignas(16) ChunkFac {
     float gam[kC], bet[kC];   // in-chunk cumulative g; beta (0 past the chunk's tokens)
