@@ -544,18 +544,12 @@ __device__ __forceinline__ void chain_fetch_v(uint32_t (&vr)[16], const uint16_t
 // Values: the output pass holds them in registers (vin; the next chunk's go to
 // vout); the map pass reads this chunk's from LDS (vl: this lane's column pair
 // of row group 0).
-template <bool WITH_V, bool WITH_OUT>
+// Output pass: one chunk of the chain from its entry state (values straight from
+// HBM into registers, outputs straight back).
 __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q, const ChunkFactors& F,
                                            f32x4 (&ST)[8][2], const uint32_t (&vin)[16], uint32_t (&vout)[16],
                                            const uint16_t* vnext, int ncn,
-                                           uint16_t* orow0, int ldv, int nc, float scale, int g, int m,
-                                           const uint32_t* vl) {
-    // Map pass: this chunk's values from LDS, requested before the products.
-    u32x4 vw[4];
-    if constexpr (WITH_V && !WITH_OUT) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) vw[mt] = *reinterpret_cast<const u32x4*>(vl + (4 * mt + g) * (D / 2) * 4);
-    }
+                                           uint16_t* orow0, int ldv, int nc, float scale, int g, int m) {
     // Z = K S^T and, for the output, Y = Q S^T: one pass over the S^T operands.
     f32x4 X[4][2], Y[4][2];
 #pragma unroll
@@ -565,60 +559,36 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
             X[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
             Y[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    if constexpr (WITH_OUT) {
-        // Software-pipelined over the key steps: step kk + 1's operand rows
-        // are requested before step kk's products are issued (the scheduler
-        // alone keeps too few LDS reads in flight here).
-        bf16x8 ka[2][4], qa[2][4];
+    // Software-pipelined over the key steps: step kk + 1's operand rows
+    // are requested before step kk's products are issued (the scheduler
+    // alone keeps too few LDS reads in flight here).
+    bf16x8 ka[2][4], qa[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        ka[0][mt] = kq_row8(K, 16 * mt + m, 0, g);
+        qa[0][mt] = kq_row8(Q, 16 * mt + m, 0, g);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int cur = kk & 1;
+        if (kk < 3) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                ka[cur ^ 1][mt] = kq_row8(K, 16 * mt + m, kk + 1, g);
+                qa[cur ^ 1][mt] = kq_row8(Q, 16 * mt + m, kk + 1, g);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 sb0 = pack_acc_pair(ST[2 * kk][0], ST[2 * kk + 1][0]);
+        const bf16x8 sb1 = pack_acc_pair(ST[2 * kk][1], ST[2 * kk + 1][1]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            ka[0][mt] = kq_row8(K, 16 * mt + m, 0, g);
-            qa[0][mt] = kq_row8(Q, 16 * mt + m, 0, g);
+            X[mt][0] = mfma16(ka[cur][mt], sb0, X[mt][0]);
+            X[mt][1] = mfma16(ka[cur][mt], sb1, X[mt][1]);
+            Y[mt][0] = mfma16(qa[cur][mt], sb0, Y[mt][0]);
+            Y[mt][1] = mfma16(qa[cur][mt], sb1, Y[mt][1]);
         }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int cur = kk & 1;
-            if (kk < 3) {
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    ka[cur ^ 1][mt] = kq_row8(K, 16 * mt + m, kk + 1, g);
-                    qa[cur ^ 1][mt] = kq_row8(Q, 16 * mt + m, kk + 1, g);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            const bf16x8 sb0 = pack_acc_pair(ST[2 * kk][0], ST[2 * kk + 1][0]);
-            const bf16x8 sb1 = pack_acc_pair(ST[2 * kk][1], ST[2 * kk + 1][1]);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                X[mt][0] = mfma16(ka[cur][mt], sb0, X[mt][0]);
-                X[mt][1] = mfma16(ka[cur][mt], sb1, X[mt][1]);
-                Y[mt][0] = mfma16(qa[cur][mt], sb0, Y[mt][0]);
-                Y[mt][1] = mfma16(qa[cur][mt], sb1, Y[mt][1]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    } else {
-        // Map pass: the same pipelining over the key steps, K only.
-        bf16x8 ka[2][4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) ka[0][mt] = kq_row8(K, 16 * mt + m, 0, g);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int cur = kk & 1;
-            if (kk < 3) {
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt) ka[cur ^ 1][mt] = kq_row8(K, 16 * mt + m, kk + 1, g);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            const bf16x8 sb0 = pack_acc_pair(ST[2 * kk][0], ST[2 * kk + 1][0]);
-            const bf16x8 sb1 = pack_acc_pair(ST[2 * kk][1], ST[2 * kk + 1][1]);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                X[mt][0] = mfma16(ka[cur][mt], sb0, X[mt][0]);
-                X[mt][1] = mfma16(ka[cur][mt], sb1, X[mt][1]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
     }
     // X = beta (V - Gamma Z); then the next chunk's values are requested.
 #pragma unroll
@@ -627,12 +597,8 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
         const f32x4 Br = *reinterpret_cast<const f32x4*>(&F.bet[16 * mt + 4 * g]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float v0 = 0.f, v1 = 0.f;
-            if (WITH_V) {
-                const uint32_t x = WITH_OUT ? vin[4 * mt + e] : vw[mt][e];
-                v0 = __uint_as_float(x << 16);
-                v1 = __uint_as_float(x & 0xFFFF0000u);
-            }
+            const uint32_t x = vin[4 * mt + e];
+            const float v0 = __uint_as_float(x << 16), v1 = __uint_as_float(x & 0xFFFF0000u);
             X[mt][0][e] = Br[e] * (v0 - Gr[e] * X[mt][0][e]);
             X[mt][1][e] = Br[e] * (v1 - Gr[e] * X[mt][1][e]);
         }
@@ -641,7 +607,7 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
     // consumed: global loads complete in order, so a load hoisted above the
     // uses of the previous ones would make those uses wait for it.
     __builtin_amdgcn_sched_barrier(0);
-    if (WITH_V && WITH_OUT) chain_fetch_v(vout, vnext, ncn, ldv, g, m);
+    chain_fetch_v(vout, vnext, ncn, ldv, g, m);
     // U by 16-row blocks: U_b = Td_b (X_b - sum A_bb' U_b'), and the state
     // update's exp(gamma_last - gamma) U_b = Tw_b (same right-hand side),
     // packed as soon as a pair of blocks is done.
@@ -673,7 +639,7 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
             Wprev[1] = w1;
         }
     }
-    if (WITH_OUT) {
+    {
         // O = scale Gamma (Q S^T) + (scale P) U
         uint32_t ob[4][4];   // bf16 pairs: row 16 mt + 4 g + e, columns cb + 2 m, cb + 2 m + 1
 #pragma unroll
@@ -699,11 +665,7 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
     }
     // S^T = Gamma_last S^T + K^T (exp(gamma_last - gamma) U)
     const float Glast = F.Gam[kChunk - 1];
-    // Map pass: recomputed every step (the empty asm hides it from loop-invariant
-    // code motion): hoisted out of the chunk loop, the sixteen addresses derived
-    // from it occupied registers for the whole loop and made the compiler spill.
-    int tro = kq_kt_tr_lane(g, m);
-    if constexpr (!WITH_OUT) asm volatile("" : "+v"(tro));
+    const int tro = kq_kt_tr_lane(g, m);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const bf16x8 a0 = kq_kt_tr(K, t, 0, tro);
@@ -717,11 +679,125 @@ __device__ __forceinline__ void chain_step(const uint16_t* K, const uint16_t* Q,
     }
 }
 
+// Map pass: the H chain (from 0, with the chunk's values) and the M chain (from I,
+// no values) advanced together over one chunk. The two chains use the same K rows,
+// factor blocks and K^T operands, so each is read from LDS once and feeds both
+// chains' products, and the two independent dependency chains interleave.
+__device__ __forceinline__ void chain_step_hm(const uint16_t* K, const ChunkFactors& F, f32x4 (&ST)[8][2],
+                                              f32x4 (&SM)[8][2], int g, int m, const uint32_t* vl) {
+    // Z = K S^T for both states, the K S^T loop software-pipelined over the key steps.
+    f32x4 XH[4][2], XM[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            XH[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            XM[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    {
+        bf16x8 ka[2][4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) ka[0][mt] = kq_row8(K, 16 * mt + m, 0, g);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int cur = kk & 1;
+            if (kk < 3) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) ka[cur ^ 1][mt] = kq_row8(K, 16 * mt + m, kk + 1, g);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 h0 = pack_acc_pair(ST[2 * kk][0], ST[2 * kk + 1][0]);
+            const bf16x8 h1 = pack_acc_pair(ST[2 * kk][1], ST[2 * kk + 1][1]);
+            const bf16x8 m0 = pack_acc_pair(SM[2 * kk][0], SM[2 * kk + 1][0]);
+            const bf16x8 m1 = pack_acc_pair(SM[2 * kk][1], SM[2 * kk + 1][1]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                XH[mt][0] = mfma16(ka[cur][mt], h0, XH[mt][0]);
+                XM[mt][0] = mfma16(ka[cur][mt], m0, XM[mt][0]);
+                XH[mt][1] = mfma16(ka[cur][mt], h1, XH[mt][1]);
+                XM[mt][1] = mfma16(ka[cur][mt], m1, XM[mt][1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // X = beta (V - Gamma Z) for H, -beta Gamma Z for M (the chunk's values from LDS).
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const u32x4 vw = *reinterpret_cast<const u32x4*>(vl + (4 * mt + g) * (D / 2) * 4);
+        const f32x4 Gr = *reinterpret_cast<const f32x4*>(&F.Gam[16 * mt + 4 * g]);
+        const f32x4 Br = *reinterpret_cast<const f32x4*>(&F.bet[16 * mt + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v0 = __uint_as_float(vw[e] << 16), v1 = __uint_as_float(vw[e] & 0xFFFF0000u);
+            XH[mt][0][e] = Br[e] * (v0 - Gr[e] * XH[mt][0][e]);
+            XH[mt][1][e] = Br[e] * (v1 - Gr[e] * XH[mt][1][e]);
+            XM[mt][0][e] = Br[e] * (0.f - Gr[e] * XM[mt][0][e]);
+            XM[mt][1][e] = Br[e] * (0.f - Gr[e] * XM[mt][1][e]);
+        }
+    }
+    // Both solves by 16-row blocks, each factor block read once for the two chains.
+    i16x4 UH[4][2], UM[4][2];
+    bf16x8 WH[2][2], WM[2][2];
+    f32x4 PH[2], PM[2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        f32x4 h0 = XH[b][0], h1 = XH[b][1], k0 = XM[b][0], k1 = XM[b][1];
+#pragma unroll
+        for (int bp = 0; bp < b; ++bp) {
+            const i16x4 a = lds_blk_a(F.Ob[b * (b - 1) / 2 + bp], g, m);
+            h0 = mfma_x16(a, UH[bp][0], h0);
+            k0 = mfma_x16(a, UM[bp][0], k0);
+            h1 = mfma_x16(a, UH[bp][1], h1);
+            k1 = mfma_x16(a, UM[bp][1], k1);
+        }
+        const i16x4 rh0 = pack4(h0), rh1 = pack4(h1), rm0 = pack4(k0), rm1 = pack4(k1);
+        const i16x4 a = lds_blk_a(F.Td[b], g, m);
+        const i16x4 aw = lds_blk_a(F.Tw[b], g, m);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        UH[b][0] = pack4(mfma_x16(a, rh0, zero));
+        UM[b][0] = pack4(mfma_x16(a, rm0, zero));
+        UH[b][1] = pack4(mfma_x16(a, rh1, zero));
+        UM[b][1] = pack4(mfma_x16(a, rm1, zero));
+        const f32x4 wh0 = mfma_x16(aw, rh0, zero), wm0 = mfma_x16(aw, rm0, zero);
+        const f32x4 wh1 = mfma_x16(aw, rh1, zero), wm1 = mfma_x16(aw, rm1, zero);
+        if (b & 1) {
+            WH[b >> 1][0] = pack_acc_pair(PH[0], wh0);
+            WH[b >> 1][1] = pack_acc_pair(PH[1], wh1);
+            WM[b >> 1][0] = pack_acc_pair(PM[0], wm0);
+            WM[b >> 1][1] = pack_acc_pair(PM[1], wm1);
+        } else {
+            PH[0] = wh0;
+            PH[1] = wh1;
+            PM[0] = wm0;
+            PM[1] = wm1;
+        }
+    }
+    // S^T = Gamma_last S^T + K^T (exp(gamma_last - gamma) U) for both states, each K^T
+    // operand read once. The lane offset is hidden from loop-invariant code motion (hoisted
+    // out of the chunk loop, the addresses derived from it would hold registers throughout).
+    const float Glast = F.Gam[kChunk - 1];
+    int tro = kq_kt_tr_lane(g, m);
+    asm volatile("" : "+v"(tro));
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const bf16x8 a0 = kq_kt_tr(K, t, 0, tro);
+        const bf16x8 a1 = kq_kt_tr(K, t, 1, tro);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            f32x4 hs = ST[t][nt] * Glast, ms = SM[t][nt] * Glast;
+            hs = mfma16(a0, WH[0][nt], hs);
+            ms = mfma16(a0, WM[0][nt], ms);
+            ST[t][nt] = mfma16(a1, WH[1][nt], hs);
+            SM[t][nt] = mfma16(a1, WM[1][nt], ms);
+        }
+    }
+}
+
 // The chain waves' chunk loop (one barrier per chunk, matching the producers).
 // Output pass: one chain with values and outputs. Map pass: the H chain (with
-// values) and, when `with_m`, the M chain (no values) for the same columns.
+// values) and the M chain (no values) for the same columns, advanced together.
 template <int MODE>
-__device__ __forceinline__ void chain_loop(SegSmem<MODE>& sm, f32x4 (&ST)[8][2], f32x4 (&SM)[8][2], bool with_m,
+__device__ __forceinline__ void chain_loop(SegSmem<MODE>& sm, f32x4 (&ST)[8][2], f32x4 (&SM)[8][2],
                                            const uint16_t* vcol, uint16_t* ocol, int64_t bos, int64_t eos,
                                            int64_t c_begin, int64_t nchunks, int ldv, float scale, int lg, int lm,
                                            int cb) {
@@ -745,22 +821,16 @@ __device__ __forceinline__ void chain_loop(SegSmem<MODE>& sm, f32x4 (&ST)[8][2],
             const int64_t cn = (i + 1 < nchunks) ? c + 1 : c;
             const int64_t t0 = bos + c * kChunk;
             const uint16_t* vnext = vcol + (bos + cn * kChunk) * ldv;
-            chain_step<true, true>(&sm.K[kb][0][0], &sm.qv.Q[kb][0][0], sm.F[i & 1], ST, va, va, vnext,
-                                   chunk_nc(cn), ocol + t0 * ldv, ldv, chunk_nc(c), scale, lg, lm, nullptr);
+            chain_step(&sm.K[kb][0][0], &sm.qv.Q[kb][0][0], sm.F[i & 1], ST, va, va, vnext, chunk_nc(cn),
+                       ocol + t0 * ldv, ldv, chunk_nc(c), scale, lg, lm);
             lds_barrier();
         }
     } else {
-        // Map pass: the H chain (values from LDS) and, when `with_m`, the M
-        // chain (no values) for the same columns.
         for (int64_t i = 0; i < nchunks; ++i) {
             const int64_t c = c_begin + i;
             const int kb = (int)(i % 3);
             const uint32_t* vl = &sm.qv.V[kb][0][cb / 2 + lm][0];
-            chain_step<true, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], ST, va, va, nullptr, 0, nullptr, ldv,
-                                    chunk_nc(c), scale, lg, lm, vl);
-            if (with_m)
-                chain_step<false, false>(&sm.K[kb][0][0], nullptr, sm.F[i & 1], SM, va, va, nullptr, 0, nullptr,
-                                         ldv, chunk_nc(c), scale, lg, lm, nullptr);
+            chain_step_hm(&sm.K[kb][0][0], sm.F[i & 1], ST, SM, lg, lm, vl);
             lds_barrier();
         }
     }
@@ -899,7 +969,7 @@ __device__ __forceinline__ void segment_body(SegSmem<MODE>& sm, const SegArgs& A
                 SM[t][nt] = e1;
             }
     }
-    chain_loop<MODE>(sm, ST, SM, MODE == kModeHM, v + h * D + cb, A.out + h * D + cb, sr.bos, sr.eos, c_begin,
+    chain_loop<MODE>(sm, ST, SM, v + h * D + cb, A.out + h * D + cb, sr.bos, sr.eos, c_begin,
                      nchunks, ldv, scale, lg, lm, cb);
 
     if (MODE == kModeOut) {
